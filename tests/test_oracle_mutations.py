@@ -1,0 +1,63 @@
+"""Plant mistakes in a copy of the oracle (on the CPU) and check the pins catch each one.
+
+A pin set that passes a broken oracle would not pin anything; every planted
+mistake below must make at least one pin fail.
+"""
+
+import os
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "tpla_oracle.py")
+
+MUTATIONS = {
+    "drop_rope_logit": ("@ c_lat[:, cols].T + rope_logits)", "@ c_lat[:, cols].T)"),
+    "drop_scale": ("logits = scale * (", "logits = 1.0 * ("),
+    "scale_only_latent": ("logits = scale * (q_tilde[:, cols] @ c_lat[:, cols].T + rope_logits)",
+                          "logits = scale * (q_tilde[:, cols] @ c_lat[:, cols].T) + rope_logits"),
+    "wrong_slice": ("cols = slice(s * w, (s + 1) * w)", "cols = slice(0, w)"),
+    "hadamard_not_symmetric": ("base = np.array([[1.0, 1.0], [1.0, -1.0]])", "base = np.array([[1.0, 1.0], [-1.0, 1.0]])"),
+    "hadamard_bad_norm": ("return h / np.sqrt(n)", "return h / n"),
+    "no_output_unrotation": ("out[b] = y @ hmat if hmat is not None else y", "out[b] = y"),
+    "no_query_rotation": ("q_tilde = q_lat[b] @ hmat if hmat is not None else q_lat[b]", "q_tilde = q_lat[b]"),
+    "lse_without_max": ("lse[b, i] = (m + np.log(z))[:, 0]", "lse[b, i] = np.log(z)[:, 0]"),
+    "no_normalisation": ("y[:, cols] = (p @ c_lat[:, cols]) / z", "y[:, cols] = (p @ c_lat[:, cols])"),
+    "max_wrong_axis": ("m = logits.max(axis=1, keepdims=True)", "m = logits.max(axis=0, keepdims=True)"),
+    "sum_wrong_axis": ("z = p.sum(axis=1, keepdims=True)", "z = p.sum(axis=0, keepdims=True)"),
+    "gather_wrong_offset": ("rows[t] = pool[page, t % page_size]", "rows[t] = pool[page, (t + 1) % page_size]"),
+    "gather_wrong_page": ("int(block_table[b][t // page_size])", "int(block_table[b][t % page_size])"),
+    "bf16_truncates": ("y = np.rint(x[finite] / quantum) * quantum", "y = np.trunc(x[finite] / quantum) * quantum"),
+    "bf16_wrong_precision": ("q_exp = np.maximum(e - 8, -133)", "q_exp = np.maximum(e - 9, -133)"),
+    "append_drops_rope": ("flat[slot, d_latent:] = rows[i, d_latent:]", "flat[slot, d_latent:] = 0.0"),
+    "append_no_rounding": ("flat[slot, :d_latent] = _store(lat, dtype)", "flat[slot, :d_latent] = lat"),
+    "shard_output_summed_not_placed": ("y[:, cols] = (p @ c_lat[:, cols]) / z", "y[:, :w] += (p @ c_lat[:, cols]) / z"),
+    "rope_from_latent": ("k_rope = rows[:, d_c:]", "k_rope = rows[:, :d_c][:, :rows.shape[1] - d_c]"),
+    "empty_lse_zero": ("lse = np.full((batch, shard_count, heads), -np.inf, dtype=np.float64)",
+                       "lse = np.full((batch, shard_count, heads), 0.0, dtype=np.float64)"),
+}
+
+
+def _mutant(name):
+    with open(SRC_PATH) as fh:
+        src = fh.read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) >= 1, f"mutation {name} no longer matches the oracle source"
+    src = src.replace(old, new)
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    mod = _mutant(name)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as exc:  # an assertion or a crash both count as caught
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin catches the planted mistake {name!r}"
