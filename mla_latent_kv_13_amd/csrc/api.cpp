@@ -1,0 +1,295 @@
+// C ABI of the latent-cache decode library: argument checks, split-K planning, workspace layout
+// and kernel launches.  Declarations and the contract of every entry point: include/tpla.h.
+#include "../../include/tpla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int32_t ok() {
+  g_last_error[0] = '\0';
+  return TPLA_OK;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(TPLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// MI355X: 256 compute units.  The split-K plan aims at a few workgroups per CU.
+constexpr int kComputeUnits = 256;
+constexpr int kMaxChunksMerge = 4096;
+
+struct Plan {
+  int kernel;        // 1 generic, 2 MFMA
+  int chunk_tokens;
+  int num_chunks;
+  size_t off_qrot, off_part_o, off_part_lse, total;
+};
+
+int32_t check_desc(const tpla_cache_desc_t* d) {
+  if (d == nullptr) return fail(TPLA_ERR_INVALID_ARGUMENT, "cache descriptor is NULL");
+  if (d->dtype != TPLA_F32 && d->dtype != TPLA_BF16) return fail(TPLA_ERR_UNSUPPORTED, "dtype %d is not fp32 or bf16", d->dtype);
+  if (d->d_latent < 1 || d->d_rope < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "d_latent must be >= 1 and d_rope >= 0");
+  if (d->page_size < 1 || d->num_pages < 1) return fail(TPLA_ERR_INVALID_ARGUMENT, "page_size and num_pages must be >= 1");
+  if (d->max_pages_per_seq < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq must be >= 0");
+  if (d->transform != TPLA_LATENT_IDENTITY && d->transform != TPLA_LATENT_WHT)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "unknown latent transform %d", d->transform);
+  const int vec = d->dtype == TPLA_BF16 ? 8 : 4;
+  if (d->d_latent % vec != 0 || d->d_rope % vec != 0)
+    return fail(TPLA_ERR_UNSUPPORTED, "d_latent and d_rope must be multiples of %d for this dtype", vec);
+  if (d->transform == TPLA_LATENT_WHT && (d->d_latent > 1024 || (d->d_latent & (d->d_latent - 1)) != 0))
+    return fail(TPLA_ERR_UNSUPPORTED, "the Hadamard transform needs d_latent a power of two <= 1024");
+  const int64_t pool_rows = static_cast<int64_t>(d->num_pages) * d->page_size;
+  if (pool_rows * (d->d_latent + d->d_rope) > (int64_t(1) << 40))
+    return fail(TPLA_ERR_UNSUPPORTED, "cache pool larger than 2^40 elements");
+  return TPLA_OK;
+}
+
+int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int32_t num_shards, int32_t shard_count,
+                  int32_t max_seq_len, const tpla_decode_opts_t* opts, Plan* plan) {
+  int32_t st = check_desc(d);
+  if (st != TPLA_OK) return st;
+  if (batch < 1 || heads < 1) return fail(TPLA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 1");
+  if (batch > 65535 || static_cast<int64_t>(heads) * shard_count > 65535)
+    return fail(TPLA_ERR_UNSUPPORTED, "batch and heads * shard_count must be <= 65535");
+  if (max_seq_len < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0");
+  if (num_shards < 1 || d->d_latent % num_shards != 0)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "num_shards=%d must be >= 1 and divide d_latent=%d", num_shards, d->d_latent);
+  if (shard_count < 1 || shard_count > num_shards)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "shard_count=%d outside [1, num_shards]", shard_count);
+  const int w = d->d_latent / num_shards;
+  const int req_kernel = opts ? opts->kernel : 0;
+  if (req_kernel < 0 || req_kernel > 2) return fail(TPLA_ERR_INVALID_ARGUMENT, "opts->kernel must be 0, 1 or 2");
+  const bool mfma_ok = d->dtype == TPLA_BF16 && tpla::mfma_supported(w, d->d_rope, heads);
+  if (req_kernel == 2 && !mfma_ok)
+    return fail(TPLA_ERR_UNSUPPORTED, "no MFMA tile for bf16 w=%d d_rope=%d heads=%d (needs w in {128,256,512}, d_rope 64, heads %% 32 == 0)",
+                w, d->d_rope, heads);
+  plan->kernel = req_kernel != 0 ? req_kernel : (mfma_ok ? 2 : 1);
+  if (plan->kernel == 1 && (w > 1024 || w + d->d_rope > 1024 + 256))
+    return fail(TPLA_ERR_UNSUPPORTED, "generic kernel supports w <= 1024 and w + d_rope <= 1280");
+
+  const int span = std::max(max_seq_len, 1);
+  int ct = opts ? opts->chunk_tokens : 0;
+  if (ct < 0 || ct % 64 != 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "chunk_tokens=%d must be 0 or a multiple of 64", ct);
+  if (ct == 0) {
+    if (plan->kernel == 2) {
+      // Workgroups per chunk index: sequences x shards x head groups of the MFMA kernel.
+      const int nw = heads % 128 == 0 ? 4 : (heads % 64 == 0 ? 2 : 1);
+      const int64_t units = static_cast<int64_t>(batch) * shard_count * (heads / (32 * nw));
+      int64_t per_seq = std::max<int64_t>(1, (2 * kComputeUnits + units - 1) / units);
+      if (d->max_pages_per_seq > 0) per_seq = std::max<int64_t>(per_seq, 16);  // ragged lengths: finer chunks balance better
+      ct = static_cast<int>(round_up((span + per_seq - 1) / per_seq, 64));
+      ct = std::max(ct, 256);
+    } else {
+      ct = static_cast<int>(std::min<int64_t>(round_up(span, 64), 1024));
+    }
+  }
+  if (plan->kernel == 1 && ct > 2048) return fail(TPLA_ERR_UNSUPPORTED, "generic kernel chunk_tokens must be <= 2048");
+  int nc = (span + ct - 1) / ct;
+  if (nc > kMaxChunksMerge) {
+    if (opts && opts->chunk_tokens) return fail(TPLA_ERR_UNSUPPORTED, "more than %d chunks per sequence", kMaxChunksMerge);
+    ct = static_cast<int>(round_up((span + kMaxChunksMerge - 1) / kMaxChunksMerge, 64));
+    nc = (span + ct - 1) / ct;
+  }
+  plan->chunk_tokens = ct;
+  plan->num_chunks = nc;
+
+  size_t off = 0;
+  plan->off_qrot = off;
+  if (d->transform == TPLA_LATENT_WHT) {
+    const size_t elem = plan->kernel == 1 ? 4 : 2;
+    off += round_up(static_cast<size_t>(batch) * heads * d->d_latent * elem, 256);
+  }
+  plan->off_part_o = off;
+  off += round_up(static_cast<size_t>(batch) * nc * shard_count * heads * static_cast<size_t>(w) * 4, 256);
+  plan->off_part_lse = off;
+  off += round_up(static_cast<size_t>(batch) * nc * shard_count * heads * 4, 256);
+  plan->total = off;
+  return TPLA_OK;
+}
+
+int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t* block_table,
+                    const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len, const void* q_latent,
+                    const void* q_rope, float scale, int32_t num_shards, int32_t shard_begin, int32_t shard_count,
+                    float* out, float* lse, void* workspace, size_t workspace_bytes, const tpla_decode_opts_t* opts,
+                    void* stream_ptr) {
+  Plan plan;
+  int32_t st = make_plan(d, batch, heads, num_shards, shard_count, max_seq_len, opts, &plan);
+  if (st != TPLA_OK) return st;
+  if (shard_begin < 0 || shard_begin + shard_count > num_shards)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "shard range [%d, %d) outside [0, %d)", shard_begin, shard_begin + shard_count, num_shards);
+  if (!cache || !seq_lens || !q_latent || !out || (d->d_rope > 0 && !q_rope))
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  if (!aligned(cache, 16) || !aligned(q_latent, 16) || (q_rope && !aligned(q_rope, 16)) || !aligned(out, 16))
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "cache, q_latent, q_rope and out must be 16-byte aligned");
+  if (!(scale == scale)) return fail(TPLA_ERR_INVALID_ARGUMENT, "scale is NaN");
+  if (block_table == nullptr) {
+    if (d->num_pages < batch || d->page_size < max_seq_len)
+      return fail(TPLA_ERR_INVALID_ARGUMENT, "without a block table sequence b uses page b: need num_pages >= batch and page_size >= max_seq_len");
+  } else {
+    if (static_cast<int64_t>(d->max_pages_per_seq) * d->page_size < max_seq_len)
+      return fail(TPLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq * page_size < max_seq_len");
+  }
+  if (plan.total > 0 && (workspace == nullptr || !aligned(workspace, 256)))
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < plan.total)
+    return fail(TPLA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, plan.total);
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const int w = d->d_latent / num_shards;
+  const bool wht = d->transform == TPLA_LATENT_WHT;
+
+  tpla::DecodeLaunch L;
+  L.cache = cache;
+  L.block_table = block_table;
+  L.seq_lens = seq_lens;
+  L.q_lat = q_latent;
+  L.q_rope = q_rope;
+  L.q_lat_f32 = d->dtype == TPLA_F32 ? 1 : 0;
+  L.scale = scale;
+  L.batch = batch;
+  L.heads = heads;
+  L.d_latent = d->d_latent;
+  L.d_rope = d->d_rope;
+  L.w = w;
+  L.page_size = d->page_size;
+  L.max_pages_per_seq = d->max_pages_per_seq;
+  L.shard_begin = shard_begin;
+  L.shard_count = shard_count;
+  L.chunk_tokens = plan.chunk_tokens;
+  L.num_chunks = plan.num_chunks;
+  L.part_o = reinterpret_cast<float*>(ws + plan.off_part_o);
+  L.part_lse = reinterpret_cast<float*>(ws + plan.off_part_lse);
+
+  hipError_t e;
+  if (wht) {
+    void* qrot = ws + plan.off_qrot;
+    const int dst_f32 = plan.kernel == 1 ? 1 : 0;
+    e = tpla::launch_rotate_query(q_latent, d->dtype == TPLA_BF16 ? 1 : 0, batch * heads, d->d_latent, qrot, dst_f32, stream);
+    if (e != hipSuccess) return hip_fail(e, "query rotation launch");
+    L.q_lat = qrot;
+    L.q_lat_f32 = dst_f32;
+  }
+  if (plan.kernel == 2) {
+    e = tpla::launch_decode_mfma(L, stream);
+    if (e != hipSuccess) return hip_fail(e, "MFMA decode launch");
+  } else {
+    e = tpla::launch_decode_generic(L, d->dtype == TPLA_BF16 ? 1 : 0, stream);
+    if (e != hipSuccess) return hip_fail(e, "generic decode launch");
+  }
+  tpla::MergeLaunch M;
+  M.part_o = L.part_o;
+  M.part_lse = L.part_lse;
+  M.seq_lens = seq_lens;
+  M.batch = batch;
+  M.heads = heads;
+  M.d_latent = d->d_latent;
+  M.w = w;
+  M.shard_begin = shard_begin;
+  M.shard_count = shard_count;
+  M.chunk_tokens = plan.chunk_tokens;
+  M.num_chunks = plan.num_chunks;
+  M.wht = wht ? 1 : 0;
+  M.out = out;
+  M.lse = lse;
+  e = tpla::launch_merge(M, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tpla_abi_version(void) { return TPLA_ABI_VERSION; }
+
+const char* tpla_status_string(int32_t status) {
+  switch (status) {
+    case TPLA_OK: return "TPLA_OK";
+    case TPLA_ERR_INVALID_ARGUMENT: return "TPLA_ERR_INVALID_ARGUMENT";
+    case TPLA_ERR_UNSUPPORTED: return "TPLA_ERR_UNSUPPORTED";
+    case TPLA_ERR_WORKSPACE_TOO_SMALL: return "TPLA_ERR_WORKSPACE_TOO_SMALL";
+    case TPLA_ERR_HIP: return "TPLA_ERR_HIP";
+    default: return "TPLA_ERR_UNKNOWN";
+  }
+}
+
+const char* tpla_last_error(void) { return g_last_error; }
+
+int32_t tpla_workspace_size(const tpla_cache_desc_t* desc, int32_t batch, int32_t heads, int32_t num_shards,
+                            int32_t shard_count, int32_t max_seq_len, const tpla_decode_opts_t* opts, size_t* bytes) {
+  if (bytes == nullptr) return fail(TPLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan plan;
+  const int32_t st = make_plan(desc, batch, heads, num_shards, shard_count, max_seq_len, opts, &plan);
+  if (st != TPLA_OK) return st;
+  *bytes = plan.total;
+  return ok();
+}
+
+int32_t latent_cache_append(const tpla_cache_desc_t* desc, void* cache, const void* rows, const int64_t* slots,
+                            int64_t n, void* stream) {
+  int32_t st = check_desc(desc);
+  if (st != TPLA_OK) return st;
+  if (n < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!cache || !rows || !slots) return fail(TPLA_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  if (!aligned(cache, 16) || !aligned(rows, 16) || !aligned(slots, 8))
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "cache and rows must be 16-byte aligned, slots 8-byte aligned");
+  if (desc->transform == TPLA_LATENT_WHT && n > 0x7fffffffLL)
+    return fail(TPLA_ERR_UNSUPPORTED, "at most 2^31-1 rows per rotated append");
+  const hipError_t e = tpla::launch_append(cache, rows, slots, n, desc->d_latent, desc->d_rope,
+                                           desc->dtype == TPLA_BF16 ? 1 : 0, desc->transform == TPLA_LATENT_WHT ? 1 : 0,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+int32_t tpla_decode_sharded(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len,
+                            const void* q_latent, const void* q_rope, float scale, int32_t num_shards,
+                            int32_t shard_begin, int32_t shard_count, float* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, cache, block_table, seq_lens, batch, heads, max_seq_len, q_latent, q_rope, scale, num_shards,
+                     shard_begin, shard_count, out, lse, workspace, workspace_bytes, nullptr, stream);
+}
+
+int32_t tpla_decode_sharded_ex(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
+                               const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len,
+                               const void* q_latent, const void* q_rope, float scale, int32_t num_shards,
+                               int32_t shard_begin, int32_t shard_count, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, const tpla_decode_opts_t* opts, void* stream) {
+  return decode_impl(desc, cache, block_table, seq_lens, batch, heads, max_seq_len, q_latent, q_rope, scale, num_shards,
+                     shard_begin, shard_count, out, lse, workspace, workspace_bytes, opts, stream);
+}
+
+int32_t mla_decode_absorbed(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len,
+                            const void* q_latent, const void* q_rope, float scale, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, cache, block_table, seq_lens, batch, heads, max_seq_len, q_latent, q_rope, scale, 1, 0, 1,
+                     out, lse, workspace, workspace_bytes, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Host-side launchers of the HIP kernels (internal to the library; the C ABI is include/tpla.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpla {
+
+// Everything a split-K decode launch needs.  Partial results of chunk c of
+// sequence b, computed shard s_local and head h live at
+//   part_o  [((b * num_chunks + c) * shard_count + s_local) * heads + h] * w   (w floats)
+//   part_lse [((b * num_chunks + c) * shard_count + s_local) * heads + h]
+// and exist only for chunks with c * chunk_tokens < seq_lens[b].
+struct DecodeLaunch {
+  const void* cache;
+  const int* block_table;
+  const int* seq_lens;
+  const void* q_lat;     // [B, H, d_c]: the caller's query, or the rotated copy in the workspace
+  const void* q_rope;    // [B, H, d_r]
+  int q_lat_f32;         // 1 when q_lat holds fp32 values (the generic kernel's rotated query)
+  float scale;
+  int batch, heads, d_latent, d_rope, w;
+  int page_size, max_pages_per_seq;
+  int shard_begin, shard_count;
+  int chunk_tokens, num_chunks;
+  float* part_o;
+  float* part_lse;
+};
+
+struct MergeLaunch {
+  const float* part_o;
+  const float* part_lse;
+  const int* seq_lens;
+  int batch, heads, d_latent, w;
+  int shard_begin, shard_count;
+  int chunk_tokens, num_chunks;
+  int wht;
+  float* out;
+  float* lse;   // may be null
+};
+
+// dtype: 0 = fp32, 1 = bf16 storage.
+hipError_t launch_decode_generic(const DecodeLaunch& a, int dtype, hipStream_t stream);
+// Returns hipErrorInvalidValue when no MFMA tile covers the shape (checked by mfma_supported first).
+bool mfma_supported(int w, int d_rope, int heads);
+hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t stream);
+hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
+// Rotate q_lat [B*H, d_c] by the Hadamard matrix into dst (fp32 if dst_f32, else bf16).
+hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_latent, void* dst, int dst_f32,
+                               hipStream_t stream);
+hipError_t launch_append(void* cache, const void* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
+                         int dtype, int wht, hipStream_t stream);
+
+}  // namespace tpla

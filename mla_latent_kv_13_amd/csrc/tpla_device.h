@@ -1,0 +1,107 @@
+// Device-side helpers shared by the HIP kernels of the latent-cache decode library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpla {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// bf16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
+
+// float -> bf16 bit pattern, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two floats -> two bf16 (round to nearest even) packed in one word, low half = a.
+// Uses the gfx950 packed conversion; the vector is read back whole, never per element.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  floatx2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T>
+__device__ __forceinline__ T store_from_f32(float v);
+template <>
+__device__ __forceinline__ float store_from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t store_from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
+
+// Block-wide reductions over blockDim.x threads (a multiple of 64); `scratch` holds >= 16 floats.
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+  v = wave_max(v);
+  const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[wv] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int i = 1; i < nw; ++i) r = fmaxf(r, scratch[i]);
+  return r;
+}
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  v = wave_sum(v);
+  const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[wv] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int i = 0; i < nw; ++i) r += scratch[i];
+  return r;
+}
+
+// In-place orthonormal Walsh-Hadamard transform of n floats in LDS (n a power of two),
+// Sylvester (natural) order: radix-2 butterflies on pairs (i, i+span) for span = 1, 2, 4, ...,
+// no bit reversal, then a 1/sqrt(n) scale.  Called by all threads of the block.
+__device__ __forceinline__ void block_fwht(float* x, int n) {
+  for (int span = 1; span < n; span <<= 1) {
+    __syncthreads();
+    for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
+      const int i = (p / span) * 2 * span + (p % span);
+      const float a = x[i], c = x[i + span];
+      x[i] = a + c;
+      x[i + span] = a - c;
+    }
+  }
+  __syncthreads();
+  const float norm = 1.0f / sqrtf(static_cast<float>(n));
+  for (int i = threadIdx.x; i < n; i += blockDim.x) x[i] *= norm;
+  __syncthreads();
+}
+
+// Row of the cache pool holding token t of sequence b.
+__device__ __forceinline__ int64_t cache_row(const int* __restrict__ block_table, int b, int t, int page_size,
+                                             int max_pages_per_seq) {
+  const int page = block_table ? block_table[static_cast<int64_t>(b) * max_pages_per_seq + t / page_size] : b;
+  return static_cast<int64_t>(page) * page_size + (t % page_size);
+}
+
+}  // namespace tpla

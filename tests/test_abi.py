@@ -1,0 +1,109 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point include/tpla.h declares,
+and rejects bad arguments on the host before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_13_amd import binding
+from mla_latent_kv_13_amd import build as build_mod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build_mod.LIB_PATH):
+        build_mod.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:int32_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("latent_cache_append", "tpla_decode_sharded", "mla_decode_absorbed", "tpla_workspace_size"):
+        assert required in names
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert binding.abi_version() == 1
+    assert lib.tpla_status_string(3) == b"TPLA_ERR_WORKSPACE_TOO_SMALL"
+
+
+DSV3 = binding.Desc("bf16", 512, 64, 64, 1000, 1024, "identity")
+
+
+def test_workspace_size_host_only(lib):
+    n = binding.workspace_size(DSV3, 16, 128, 2, 2, 32768)
+    assert n > 16 * 2 * 128 * 256 * 4  # at least one chunk of partials per sequence and shard
+    rot = binding.Desc("bf16", 512, 64, 64, 1000, 1024, "wht")
+    assert binding.workspace_size(rot, 16, 128, 2, 2, 32768) > n  # room for the rotated query
+    assert binding.workspace_size(DSV3, 16, 128, 2, 2, 32768, chunk_tokens=64) > n
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(num_shards=3), "INVALID_ARGUMENT"),            # 3 does not divide 512
+    (dict(num_shards=2, shard_count=3), "INVALID_ARGUMENT"),
+    (dict(heads=0), "INVALID_ARGUMENT"),
+    (dict(chunk_tokens=100), "INVALID_ARGUMENT"),
+    (dict(kernel="mfma", heads=40), "UNSUPPORTED"),
+])
+def test_workspace_size_rejects(lib, kw, msg):
+    args = dict(batch=2, heads=128, num_shards=2, shard_count=None, max_seq_len=4096, chunk_tokens=0, kernel="auto")
+    args.update(kw)
+    if args["shard_count"] is None:
+        args["shard_count"] = args["num_shards"]
+    with pytest.raises(binding.TplaError, match=msg):
+        binding.workspace_size(DSV3, args["batch"], args["heads"], args["num_shards"], args["shard_count"],
+                               args["max_seq_len"], args["chunk_tokens"], args["kernel"])
+
+
+def _decode_raw(lib, desc, **kw):
+    """Call tpla_decode_sharded with fake (never dereferenced) device addresses; only for
+    arguments that validation rejects before anything is enqueued."""
+    a = dict(cache=0x10000, block_table=0x20000, seq_lens=0x30000, batch=2, heads=128, max_seq_len=4096,
+             q_latent=0x40000, q_rope=0x50000, scale=0.1, num_shards=2, shard_begin=0, shard_count=2,
+             out=0x60000, lse=0, workspace=0x70000, workspace_bytes=1 << 40)
+    a.update(kw)
+    cdesc = desc.c()
+    p = ctypes.c_void_p
+    st = lib.tpla_decode_sharded(ctypes.byref(cdesc), p(a["cache"]), p(a["block_table"] or None), p(a["seq_lens"]),
+                                 a["batch"], a["heads"], a["max_seq_len"], p(a["q_latent"]), p(a["q_rope"]),
+                                 ctypes.c_float(a["scale"]), a["num_shards"], a["shard_begin"], a["shard_count"],
+                                 p(a["out"]), p(a["lse"] or None), p(a["workspace"]), a["workspace_bytes"], None)
+    return st, lib.tpla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cache=0), 1),
+    (dict(out=0x60004), 1),                      # misaligned output
+    (dict(shard_begin=1, shard_count=2), 1),     # shard range beyond G
+    (dict(num_shards=5, shard_count=5), 1),      # G does not divide d_latent
+    (dict(workspace_bytes=16), 3),
+    (dict(scale=float("nan")), 1),
+    (dict(block_table=0, max_seq_len=4096), 1),  # no block table needs page_size >= max_seq_len
+])
+def test_decode_validation_before_launch(lib, kw, status):
+    st, msg = _decode_raw(lib, DSV3, **kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_bad_descriptor(lib):
+    bad = binding.Desc("bf16", 768, 64, 64, 10, 16, "wht")  # Hadamard needs a power of two
+    st, msg = _decode_raw(lib, bad)
+    assert st == 2 and "power of two" in msg
+    odd = binding.Desc("bf16", 512, 60, 64, 10, 16, "identity")  # 60 is not a multiple of 8
+    st, msg = _decode_raw(lib, odd)
+    assert st == 2
