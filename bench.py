@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of latent-cache decode (weight-absorbed MLA / TPLA) on one MI355X.
+
+One step = one decode call through the C ABI over one batch of the workload (the
+query rotation when the cache is Hadamard-rotated, the split-K decode kernel and the
+log-sum-exp merge / shard sum), with the cache, block table and queries resident in
+HBM.  Before every step, timed or not, a 1 GiB buffer is overwritten so that no
+part of the cache survives in the 256 MB last-level cache: the figures are HBM
+figures.  Steps are timed with HIP events on the call's stream; the split-K decode
+kernel is also timed alone with events the library records around it.
+
+Cache eviction reads a 1 GiB buffer (a reduction with a scalar result): reading leaves only
+clean lines behind, whereas overwriting a buffer would leave up to 256 MB of dirty lines whose
+write-back then competes with the timed kernel's reads.
+
+Prints ONE JSON line.  The headline workload is the DeepSeek-V3-shaped exact MLA
+decode (G = 1, batch 32, 128 heads, latent 512 + rope 64, context 4096, bf16);
+the other workloads (TPLA G = 2 / G = 4 at 32K context, paged + Hadamard with
+ragged contexts) are reported in "workloads" unless --headline-only is given.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "latent-cache decode tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_13_amd", "csrc", "decode_mfma.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5], help="headline workload")
+    p.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    p.add_argument("--extra-steps", type=int, default=10, help="timed steps of each other workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--chunk-tokens", type=int, default=0)
+    p.add_argument("--no-flush", action="store_true", help="do not evict the last-level cache between steps")
+    return p.parse_args()
+
+
+class Workload:
+    """Device-resident inputs of one seeded workload plus preallocated outputs and workspace."""
+
+    def __init__(self, cfg: int, chunk_tokens: int = 0):
+        import numpy as np
+        import torch
+
+        from mla_latent_kv_13_amd import binding, inputs
+
+        self.cfg = cfg
+        t0 = time.time()
+        case = inputs.make_config(cfg)
+        self.case = case
+        dev = "cuda:0"
+
+        def dev_t(a):
+            if case.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+        self.desc = binding.Desc(case.dtype, case.d_latent, case.d_rope, case.page_size, case.num_pages,
+                                 case.max_pages_per_seq, case.transform)
+        self.q_lat = dev_t(case.q_lat)
+        self.q_rope = dev_t(case.q_rope)
+        self.seq_lens = torch.from_numpy(case.seq_lens).to(dev)
+        self.block_table = None if case.block_table is None else torch.from_numpy(case.block_table).to(dev)
+        if case.transform == "identity":
+            self.pool = dev_t(case.pool)
+        else:
+            self.pool = dev_t(case.empty_pool())
+            rows = dev_t(case.rows)
+            slots = torch.from_numpy(case.slots).to(dev)
+            binding.latent_cache_append(self.desc, self.pool, rows, slots)
+            torch.cuda.synchronize()
+            del rows, slots
+        self.chunk_tokens = chunk_tokens
+        B, H = case.batch, case.heads
+        self.out = torch.empty((B, H, case.d_latent), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, case.shards, H), dtype=torch.float32, device=dev)
+        need = binding.workspace_size(self.desc, B, H, case.shards, case.shards, case.max_seq_len, chunk_tokens)
+        self.workspace = binding.alloc_workspace(need, dev)
+        self.tokens = case.total_tokens
+        elem = 2 if case.dtype == "bf16" else 4
+        self.bytes = self.tokens * (case.d_latent + case.d_rope) * elem
+        self.binding = binding
+        log(f"workload {cfg} ({case.name}): {self.tokens} cached tokens, {self.bytes / 1e6:.1f} MB, "
+            f"prepared in {time.time() - t0:.1f}s")
+
+    def call(self, events=None):
+        c = self.case
+        self.binding.tpla_decode_sharded(self.desc, self.pool, self.block_table, self.seq_lens, self.q_lat,
+                                         self.q_rope, c.scale, c.shards, c.max_seq_len, out=self.out, lse=self.lse,
+                                         workspace=self.workspace, chunk_tokens=self.chunk_tokens, events=events)
+
+    def config(self):
+        c = self.case
+        d = {"workload": c.name, "batch": c.batch, "heads": c.heads, "d_latent": c.d_latent, "d_rope": c.d_rope,
+             "shards": c.shards, "dtype": c.dtype, "transform": c.transform,
+             "layout": "paged" if c.paged else "contiguous", "cached_tokens": self.tokens}
+        if c.paged:
+            d.update(page_size=c.page_size, context="uniform[1024,65536]", max_seq_len=c.max_seq_len)
+        else:
+            d.update(context=c.max_seq_len)
+        return d
+
+
+def time_workload(w: Workload, steps: int, warmup: int, flush: bool):
+    import torch
+
+    flush_buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda:0") if flush else None
+
+    def evict():
+        if flush_buf is not None:
+            flush_buf.sum()
+
+    for _ in range(warmup):
+        evict()
+        w.call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evict()
+        ev[i][0].record()
+        w.call(events=(ev[i][1], ev[i][2]))
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [e[0].elapsed_time(e[3]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    mean_call = statistics.fmean(call_ms)
+    mean_dec = statistics.fmean(dec_ms)
+    return {
+        "call_ms_mean": mean_call, "call_ms_median": statistics.median(call_ms), "call_ms_min": min(call_ms),
+        "decode_kernel_ms_mean": mean_dec, "decode_kernel_ms_min": min(dec_ms),
+        "tokens_per_s": w.tokens / (mean_call * 1e-3),
+        "call_gbs": w.bytes / (mean_call * 1e-3) / 1e9,
+        "decode_kernel_gbs": w.bytes / (mean_dec * 1e-3) / 1e9,
+        "wall_s_with_flush": wall,
+    }
+
+
+def traffic_for_current_kernel(workload_name: str):
+    """HBM bytes per decode-kernel launch from the committed counter summary, if it was taken
+    on the kernel source as it stands now (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+        with open(KERNEL_SRC, "rb") as fh:
+            digest = hashlib.sha256(fh.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload_name)
+    if entry is None or rec.get("decode_mfma_sha256") != digest:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(c, budget_s: float = 20.0):
+    """The fp64 oracle on the host cores, on whole sequences of the headline workload, repeated
+    over the batch until about budget_s of work (decode computation only)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from mla_latent_kv_13_amd import inputs
+
+    pool = inputs.stored_to_f64(c.pool, c.dtype) if c.pool is not None else None
+    if pool is None:
+        return None
+    q_lat = inputs.stored_to_f64(c.q_lat, c.dtype)
+    q_rope = inputs.stored_to_f64(c.q_rope, c.dtype)
+    done_tokens, spent, seqs = 0, 0.0, 0
+    b = 0
+    while spent < budget_s and seqs < 4 * c.batch:
+        t0 = time.perf_counter()
+        oracle.tpla_decode_sharded(pool[b:b + 1], None if c.block_table is None else c.block_table[b:b + 1],
+                                   c.seq_lens[b:b + 1], q_lat[b:b + 1], q_rope[b:b + 1], c.scale, c.shards,
+                                   transform=c.transform)
+        spent += time.perf_counter() - t0
+        done_tokens += int(c.seq_lens[b])
+        seqs += 1
+        b = (b + 1) % c.batch
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": done_tokens / spent, "unit": "cache-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{seqs} whole sequences ({done_tokens} cached tokens) of the {c.name} workload, "
+                      f"fp64 NumPy oracle, {spent:.1f}s; host has {len(os.sched_getaffinity(0))} usable cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("bench.py measures the single-GPU hot path; multi-GPU runs are not part of this build")
+        sys.exit(2)
+    import torch
+
+    from mla_latent_kv_13_amd import binding
+
+    binding.load_library()
+    torch.cuda.init()
+    head = Workload(args.config, args.chunk_tokens)
+    res = time_workload(head, args.steps, args.warmup, not args.no_flush)
+    log(f"headline: {json.dumps(res)}")
+    traffic = traffic_for_current_kernel(head.case.name)
+    dec_gbs = res["decode_kernel_gbs"]
+    line = {
+        "metric": METRIC,
+        "value": res["tokens_per_s"],
+        "unit": "cache-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["call_ms_mean"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.case.dtype,
+        "data": "synthetic (seeded N(0,1) queries and cache rows of the workload's shapes)",
+        "config": head.config(),
+        "hbm_gbs": res["call_gbs"],
+        "hbm_frac_of_peak": res["call_gbs"] / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "split-K decode kernel (decode_mfma_kernel)",
+                     "algorithmic_bytes_per_launch": head.bytes,
+                     "kernel_ms_mean": res["decode_kernel_ms_mean"]},
+        "timing": res,
+    }
+    head_case = head.case
+    del head
+    torch.cuda.empty_cache()
+    if not args.headline_only:
+        others = {}
+        for cfg in (2, 3, 4, 5):
+            if cfg == args.config:
+                continue
+            w = Workload(cfg, args.chunk_tokens)
+            r = time_workload(w, args.extra_steps, 2, not args.no_flush)
+            others[w.case.name] = {"config": w.config(), "tokens_per_s": r["tokens_per_s"],
+                                   "call_ms_mean": r["call_ms_mean"], "hbm_gbs": r["call_gbs"],
+                                   "hbm_frac_of_peak": r["call_gbs"] / HBM_PEAK_GBS,
+                                   "decode_kernel_gbs": r["decode_kernel_gbs"],
+                                   "decode_kernel_frac_of_peak": r["decode_kernel_gbs"] / HBM_PEAK_GBS,
+                                   "traffic": traffic_for_current_kernel(w.case.name)}
+            log(f"workload {cfg}: {json.dumps(others[w.case.name])}")
+            del w
+            torch.cuda.empty_cache()
+        line["workloads"] = others
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(head_case)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -88,17 +88,22 @@ typedef struct {
   int32_t transform;         /* tpla_transform_t                                            */
 } tpla_cache_desc_t;
 
-/* Optional tuning of a decode call (NULL = library defaults).
+/* Optional tuning and timing of a decode call (NULL = library defaults).
  * chunk_tokens: tokens per split-K chunk (the context of each sequence is cut
  *   into chunks processed by separate workgroups and merged exactly by
  *   log-sum-exp, [FR] Directions: sequence split with a log-sum-exp merge);
  *   0 = library choice, else a multiple of 64.
  * kernel: 0 = library choice; 1 = the generic VALU kernel (any supported
  *   shape, fp32 or bf16); 2 = the bf16 MFMA kernel (UNSUPPORTED when the shape
- *   has no MFMA tile). */
+ *   has no MFMA tile).
+ * decode_begin, decode_end: hipEvent_t handles (as void*) recorded on the
+ *   call's stream immediately before and after the split-K decode kernel, or
+ *   NULL; they time that kernel alone. */
 typedef struct {
   int32_t chunk_tokens;
   int32_t kernel;
+  void* decode_begin;
+  void* decode_end;
 } tpla_decode_opts_t;
 
 int32_t     tpla_abi_version(void);

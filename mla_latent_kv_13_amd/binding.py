@@ -41,7 +41,8 @@ class CacheDesc(ctypes.Structure):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("chunk_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+    _fields_ = [("chunk_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("decode_begin", ctypes.c_void_p), ("decode_end", ctypes.c_void_p)]
 
 
 @dataclass(frozen=True)
@@ -118,10 +119,20 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _opts(chunk_tokens: int = 0, kernel: str = "auto"):
-    if not chunk_tokens and kernel == "auto":
+def _event_handle(ev):
+    """Raw hipEvent_t of a torch.cuda.Event (recorded once so that it exists)."""
+    if ev is None:
         return None
-    return ctypes.byref(DecodeOpts(int(chunk_tokens), KERNELS[kernel]))
+    if not ev.cuda_event:
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
+
+
+def _opts(chunk_tokens: int = 0, kernel: str = "auto", events=None):
+    if not chunk_tokens and kernel == "auto" and events is None:
+        return None
+    begin, end = events if events is not None else (None, None)
+    return ctypes.byref(DecodeOpts(int(chunk_tokens), KERNELS[kernel], _event_handle(begin), _event_handle(end)))
 
 
 def abi_version() -> int:
@@ -159,8 +170,11 @@ def tpla_decode_sharded(desc: Desc, cache: torch.Tensor, block_table: torch.Tens
                         max_seq_len: int, shard_begin: int = 0, shard_count: int | None = None,
                         out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, want_lse: bool = True,
-                        chunk_tokens: int = 0, kernel: str = "auto", stream=None):
-    """TPLA decode; returns (out [B, H, d_latent] fp32, lse [B, shard_count, H] fp32 or None)."""
+                        chunk_tokens: int = 0, kernel: str = "auto", events=None, stream=None):
+    """TPLA decode; returns (out [B, H, d_latent] fp32, lse [B, shard_count, H] fp32 or None).
+
+    ``events=(begin, end)`` (torch.cuda.Event with timing) are recorded around the split-K
+    decode kernel alone."""
     if shard_count is None:
         shard_count = num_shards - shard_begin
     batch, heads = int(q_latent.shape[0]), int(q_latent.shape[1])
@@ -179,7 +193,7 @@ def tpla_decode_sharded(desc: Desc, cache: torch.Tensor, block_table: torch.Tens
     _check(lib.tpla_decode_sharded_ex(ctypes.byref(cdesc), _ptr(cache), _ptr(block_table), _ptr(seq_lens), batch, heads,
                                       max_seq_len, _ptr(q_latent), _ptr(q_rope), ctypes.c_float(scale), num_shards,
                                       shard_begin, shard_count, _ptr(out), _ptr(lse), _ptr(workspace),
-                                      workspace.numel(), _opts(chunk_tokens, kernel), _stream(stream)))
+                                      workspace.numel(), _opts(chunk_tokens, kernel, events), _stream(stream)))
     return out, lse
 
 

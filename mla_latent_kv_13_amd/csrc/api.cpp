@@ -94,10 +94,14 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
   if (ct < 0 || ct % 64 != 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "chunk_tokens=%d must be 0 or a multiple of 64", ct);
   if (ct == 0) {
     if (plan->kernel == 2) {
-      // Workgroups per chunk index: sequences x shards x head groups of the MFMA kernel.
-      const int nw = heads % 128 == 0 ? 4 : (heads % 64 == 0 ? 2 : 1);
-      const int64_t units = static_cast<int64_t>(batch) * shard_count * (heads / (32 * nw));
-      int64_t per_seq = std::max<int64_t>(1, (2 * kComputeUnits + units - 1) / units);
+      // One round of workgroups fills the chip: chunks per sequence so that
+      // sequences x chunks x shards x head groups = CUs x workgroups per CU.  Fewer, longer chunks
+      // keep the split-K partials (heads x d_latent fp32 per chunk) small next to the cache bytes.
+      int head_groups = 1, per_cu = 1;
+      tpla::mfma_plan_info(w, heads, &head_groups, &per_cu);
+      const int64_t per_index = static_cast<int64_t>(batch) * shard_count * head_groups;
+      const int64_t slots = static_cast<int64_t>(kComputeUnits) * per_cu;
+      int64_t per_seq = std::max<int64_t>(1, (slots + per_index - 1) / per_index);
       if (d->max_pages_per_seq > 0) per_seq = std::max<int64_t>(per_seq, 16);  // ragged lengths: finer chunks balance better
       ct = static_cast<int>(round_up((span + per_seq - 1) / per_seq, 64));
       ct = std::max(ct, 256);
@@ -106,6 +110,14 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
     }
   }
   if (plan->kernel == 1 && ct > 2048) return fail(TPLA_ERR_UNSUPPORTED, "generic kernel chunk_tokens must be <= 2048");
+  if (plan->kernel == 2 && d->max_pages_per_seq > 0) {
+    // a chunk's block-table entries are staged in LDS
+    const int max_ct = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(tpla::mfma_max_chunk_pages() - 1) * d->page_size, 1 << 30));
+    if (ct > max_ct) {
+      if (opts && opts->chunk_tokens) return fail(TPLA_ERR_UNSUPPORTED, "chunk_tokens spans more cache pages than the kernel stages");
+      ct = std::max(64, max_ct / 64 * 64);
+    }
+  }
   int nc = (span + ct - 1) / ct;
   if (nc > kMaxChunksMerge) {
     if (opts && opts->chunk_tokens) return fail(TPLA_ERR_UNSUPPORTED, "more than %d chunks per sequence", kMaxChunksMerge);
@@ -192,12 +204,20 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
     L.q_lat = qrot;
     L.q_lat_f32 = dst_f32;
   }
+  if (opts && opts->decode_begin) {
+    e = hipEventRecord(static_cast<hipEvent_t>(opts->decode_begin), stream);
+    if (e != hipSuccess) return hip_fail(e, "recording decode_begin");
+  }
   if (plan.kernel == 2) {
     e = tpla::launch_decode_mfma(L, stream);
     if (e != hipSuccess) return hip_fail(e, "MFMA decode launch");
   } else {
     e = tpla::launch_decode_generic(L, d->dtype == TPLA_BF16 ? 1 : 0, stream);
     if (e != hipSuccess) return hip_fail(e, "generic decode launch");
+  }
+  if (opts && opts->decode_end) {
+    e = hipEventRecord(static_cast<hipEvent_t>(opts->decode_end), stream);
+    if (e != hipSuccess) return hip_fail(e, "recording decode_end");
   }
   tpla::MergeLaunch M;
   M.part_o = L.part_o;

@@ -1,187 +1,519 @@
 // bf16 split-K TPLA decode on the gfx950 matrix cores.
 //
-// Work unit: one workgroup = (token chunk c, sequence b, shard s, group of 32*NW heads).  It
-// streams the chunk's cache rows of that shard -- the latent slice [s*W, (s+1)*W) and the whole
-// rope key, i.e. the per-device share of the TPLA review page (320 = 256 + 64 values per token
-// at two shards) -- from HBM into double-buffered LDS tiles of 32 tokens.  Every wave owns 32
-// heads and, per tile:
-//   S^T[token, head] = K_tile[token, :] . Q^T[:, head]       32x32x16 bf16 MFMA, K = W + D_R
-//   online softmax over tokens per head (per-lane partials, one cross-half max per tile)
-//   O^T[col, head]  += V_tile^T[col, token] . P^T[token, head]  32x32x16 bf16 MFMA, K = tokens
-// with the value tile read transposed out of LDS by ds_read_b64_tr_b16.  The chunk's normalised
-// output and log-sum-exp go to the workspace; the merge kernel combines chunks exactly
-// (feature request on latent-cache sharding, "Directions under investigation": sequence split
-// plus log-sum-exp merge).  The slice softmax is plain, with the same scale on every shard
-// (TPLA abstract; review page, Eq. 6).
+// Work unit: one workgroup = (token chunk, sequence b, shard s, group of 32*HB heads).  It streams
+// the chunk's cache rows of that shard -- the latent slice [s*W, (s+1)*W) and the whole rope key,
+// the per-device share of the TPLA review page (320 = 256 + 64 values per token at two shards) --
+// from HBM straight into a ring of ST LDS tiles of 32 tokens with global_load_lds_dwordx4 (no
+// register staging), keeping ST-1 tiles in flight per workgroup so that enough bytes are
+// outstanding to cover HBM latency.  Per tile, every wave owns 32 heads and:
+//   S^T[token, head] = K_tile[token, :] . Q^T[:, head]        32x32x16 bf16 MFMA over key width
+//   online softmax over tokens per head, in base 2
+//   O^T[col, head]  += V_tile^T[col, token] . P^T[token, head]  32x32x16 bf16 MFMA over tokens
+// with the value tile read transposed out of LDS by ds_read_b64_tr_b16.  With KS = 2 the two waves
+// of a pair split the key width for S (exchanging fp32 partial logits through LDS) and the value
+// columns for O, which halves the registers each wave needs for the wide single-shard case.
+// The chunk's normalised output and log-sum-exp go to the workspace and the merge kernel combines
+// chunks exactly (feature request on latent-cache sharding, "Directions under investigation":
+// sequence split plus log-sum-exp merge).  The slice softmax is plain, with the same scale on
+// every shard (TPLA abstract; review page, Eq. 6).
 //
 // Lane layouts (checked on gfx950): for v_mfma_f32_32x32x16_bf16 lane l holds A[l%32][8*(l/32)+i]
 // and B[8*(l/32)+i][l%32], i = 0..7, and accumulator j of lane l is D[8*(j/4)+4*(l/32)+j%4][l%32].
 // ds_read_b64_tr_b16 lets lane q of each 16-lane group address row q/4, columns 4*(q%4)..+3 of a
-// 4 x 16 block and returns column q (rows 0..3).
+// 4 x 16 block and returns column q (rows 0..3).  global_load_lds_dwordx4 writes lane i's 16 bytes
+// at LDS base + 16*i, so a tile is laid out in 1 KiB pieces, one per wave instruction.
+//
+// LDS tile layout: token-major rows of KW bf16 (KW = W + D_R) in 16-byte chunks; chunk c of token t
+// sits at position c ^ f(t), f(t) = 2*(t%4) + (t/4)%2 (a permutation within each group of 8
+// chunks).  Eight consecutive tokens reading the same chunk (the K operand) then hit eight
+// different 16-byte bank groups, and so do four consecutive tokens reading two adjacent chunks
+// (the transposed V operand).
+//
+// Cache layouts: LAYOUT 0 = contiguous (sequence b owns rows b*page_size...), 1 = paged with
+// page_size a multiple of 32 (a tile never straddles a page), 2 = any other paging.  In layouts
+// 0 and 1 a full tile is 32 consecutive rows, so each lane's DMA source is a fixed byte offset
+// from one wave-uniform row address.
+#include <type_traits>
+
 #include "kernels.h"
 #include "tpla_device.h"
 
 namespace tpla {
 namespace {
 
-constexpr int kNT = 32;  // tokens per LDS tile (the M dimension of the QK product)
+constexpr int kNT = 32;          // tokens per LDS tile (the M dimension of the QK product)
+constexpr int kMaxPages = 1024;  // block-table entries of one chunk kept in LDS
 
-template <int W, int DR, int NW>
-struct Cfg {
-  static constexpr int KW = W + DR;                    // key width of one shard
-  static constexpr int KSTEPS = KW / 16;               // 16-deep MFMA steps of the QK product
-  static constexpr int ROW_BYTES = KW * 2 + 16;        // LDS row pitch: 16 B of padding spreads banks
-  static constexpr int TILE_BYTES = kNT * ROW_BYTES;
-  static constexpr int CPR = KW / 8;                   // 16-byte chunks per row
-  static constexpr int LAT_CPR = W / 8;
-  static constexpr int THREADS = NW * 64;
-  static constexpr int LOADS = (kNT * CPR + THREADS - 1) / THREADS;
-  static constexpr int CB = W / 32;                    // 32-column blocks of the value
-  static constexpr int LDS_BYTES = 2 * TILE_BYTES;
-  static_assert(W % 32 == 0 && DR % 16 == 0, "tile shape");
-};
-
+typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-template <int W, int DR, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeLaunch a, float scale_log2) {
-  using C = Cfg<W, DR, NW>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+template <int W, int DR, int HB, int KS, int STQ>
+struct Cfg {
+  static constexpr int KW = W + DR;                // key width of one shard
+  static constexpr int ROW_BYTES = KW * 2;
+  static constexpr int CPR = KW / 8;               // 16-byte chunks per token row
+  static constexpr int LAT_CPR = W / 8;
+  static constexpr int TILE_BYTES = kNT * ROW_BYTES;
+  static constexpr int NWAVES = HB * KS;
+  static constexpr int THREADS = NWAVES * 64;
+  static constexpr int INSTR = kNT * CPR / 64;     // 1 KiB DMA pieces per tile
+  static constexpr int PER_LO = INSTR / NWAVES;    // pieces per wave; the first REM waves take one more
+  static constexpr int REM = INSTR % NWAVES;
+  static constexpr int PER_MAX = PER_LO + (REM ? 1 : 0);
+  // ring stages: as requested, but never more loads in flight per lane than vmcnt can count (63)
+  static constexpr int ST = STQ < 2 + 63 / PER_MAX ? STQ : 2 + 63 / PER_MAX;
+  static constexpr int KSTEPS = KW / 16 / KS;      // QK k-steps of one wave
+  static constexpr int CB = W / 32 / KS;           // 32-column value blocks of one wave
+  static constexpr int SX_OFF = ST * TILE_BYTES;   // partial-logit exchange (KS > 1)
+  static constexpr int SX_BYTES = KS > 1 ? 2 * NWAVES * 4096 : 0;  // double-buffered by tile parity
+  static constexpr int PAGES_OFF = SX_OFF + SX_BYTES;
+  static constexpr int LDS_BYTES = PAGES_OFF + kMaxPages * 4;
+  static_assert(W % 32 == 0 && DR % 16 == 0 && CPR % 8 == 0, "tile shape");
+  static_assert(kNT * CPR % 64 == 0, "a tile is a whole number of 1 KiB pieces");
+  static_assert((KW / 16) % KS == 0 && (W / 32) % KS == 0, "key/value split");
+  static_assert(KS == 1 || KS == 2, "key split");
+  static_assert(ST >= 3, "ring of at least three tiles (two resident, one in flight)");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
 
-  const int c = blockIdx.x, b = blockIdx.y;
-  const int groups = a.heads / (32 * NW);
-  const int s_local = blockIdx.z / groups, hg = blockIdx.z % groups;
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7
+// meaning no wait, lgkmcnt [11:8] = 0).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// One 16-byte-per-lane LDS DMA: lane i's 16 bytes land at LDS byte `lds_base + 16*i` (the
+// wave-uniform base goes through M0).  Issued from asm so that the compiler does not treat every
+// later LDS read as possibly aliasing it and wait for it (it would insert vmcnt(0) before the
+// first read of the tile being computed and serialise the ring); the instruction has no
+// destination register -- its data goes to LDS -- and completion is awaited explicitly with
+// s_waitcnt vmcnt before the barrier that publishes the tile.
+// Source = 64-bit per-lane address:
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+// Source = wave-uniform 64-bit base (SGPRs) + per-lane 32-bit byte offset:
+__device__ __forceinline__ void dma16_sbase(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Workgroup barrier without a memory fence: LDS-DMA loads stay in flight across it (the caller
+// has already waited for the ones it needs), and the empty asm keeps the compiler from moving
+// memory accesses over it.
+__device__ __forceinline__ void raw_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
+__global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaunch a, float scale_log2, int units,
+                                                                       int members, int page_shift) {
+  using C = Cfg<W, DR, HB, KS, STQ>;
+  constexpr int ST = C::ST;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+
+  // XCD-aware placement: consecutive workgroups go to the 8 XCDs in turn, so the members of one
+  // unit (its shards and head groups, which read the same tokens) take ids 8 apart: same XCD,
+  // adjacent in dispatch order, sharing that XCD's L2 for the common rows.
+  const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+  const int member = slot % members;
+  const int u = (slot / members) * 8 + xcd;
+  if (u >= units) return;
+  const int c = u % a.num_chunks, b = u / a.num_chunks;
+  const int groups = a.heads / (32 * HB);
+  const int s_local = member / groups, hg = member % groups;
   const int s = a.shard_begin + s_local;
   const int T = a.seq_lens[b];
   const int t_begin = c * a.chunk_tokens;
   if (t_begin >= T) return;
   const int t_end = min(T, t_begin + a.chunk_tokens);
+  const int n_tiles = (t_end - t_begin + kNT - 1) / kNT;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hb = wv / KS, kh = wv % KS;
   const int half = lane >> 5, l32 = lane & 31;
-  const int head = (hg * NW + wv) * 32 + l32;
+  const int head = (hg * HB + hb) * 32 + l32;
   const int d_c = a.d_latent;
   const int64_t D = d_c + DR;
-  const uint16_t* __restrict__ cache = static_cast<const uint16_t*>(a.cache);
+  const unsigned char* __restrict__ cache = static_cast<const unsigned char*>(a.cache);
+  const int page_size = a.page_size;
 
-  // Q^T operand of the QK product: lane holds features 16*kk + 8*half .. +7 of its head.
+  int* pages = reinterpret_cast<int*>(lds + C::PAGES_OFF);
+  const int first_page = LAYOUT ? (page_shift >= 0 ? (t_begin >> page_shift) : t_begin / page_size) : 0;
+  if constexpr (LAYOUT != 0) {
+    const int last_page = page_shift >= 0 ? ((t_end - 1) >> page_shift) : (t_end - 1) / page_size;
+    const int* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages_per_seq + first_page;
+    for (int i = tid; i <= last_page - first_page; i += C::THREADS) pages[i] = bt[i];
+  }
+  __syncthreads();
+
+  // This wave's DMA pieces are [first_piece, first_piece + n_pieces); piece k covers tile slots
+  // k*64 + lane; slot -> (token tt, position p) -> source chunk p ^ f(tt).  dofs[k] is the lane's
+  // byte offset from the tile's first row when the tile is 32 consecutive rows.
+  const int n_pieces = C::PER_LO + (wv < C::REM ? 1 : 0);
+  const int first_piece = wv * C::PER_LO + min(wv, C::REM);
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds)) + first_piece * 1024);
+  uint32_t dofs[C::PER_MAX];
+#pragma unroll
+  for (int k = 0; k < C::PER_MAX; ++k) {
+    const int sigma = (first_piece + k) * 64 + lane;
+    const int tt = sigma / C::CPR, p = sigma % C::CPR;
+    const int ch = p ^ swz(tt);
+    const int col = (ch < C::LAT_CPR) ? s * W + ch * 8 : d_c + (ch - C::LAT_CPR) * 8;
+    dofs[k] = static_cast<uint32_t>(tt * D * 2 + col * 2);
+  }
+  // Byte address of cache row `row`.
+  auto row_addr = [&](int64_t row) { return cache + row * D * 2; };
+  auto row_of = [&](int t) -> int64_t {
+    if constexpr (LAYOUT == 0) {
+      return static_cast<int64_t>(b) * page_size + t;
+    } else {
+      const int pi = page_shift >= 0 ? (t >> page_shift) : t / page_size;
+      const int off = page_shift >= 0 ? (t & (page_size - 1)) : t - pi * page_size;
+      return static_cast<int64_t>(pages[pi - first_page]) * page_size + off;
+    }
+  };
+
+  auto issue = [&](int j, int stage) {
+    const int t0 = t_begin + j * kNT;
+    const uint32_t dst = lds_base + stage * C::TILE_BYTES;
+    if (LAYOUT != 2 && t0 + kNT <= t_end) {
+      // 32 consecutive rows: one uniform base, per-lane constant offsets
+      const void* base = uniform_ptr(row_addr(row_of(t0)));
+#pragma unroll
+      for (int k = 0; k < C::PER_MAX; ++k) {
+        if (C::REM != 0 && k >= n_pieces) break;
+        dma16_sbase(dofs[k], base, dst + k * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < C::PER_MAX; ++k) {
+        if (C::REM != 0 && k >= n_pieces) break;
+        const int sigma = (first_piece + k) * 64 + lane;
+        const int tt = sigma / C::CPR, p = sigma % C::CPR;
+        const int ch = p ^ swz(tt);
+        const int col = (ch < C::LAT_CPR) ? s * W + ch * 8 : d_c + (ch - C::LAT_CPR) * 8;
+        const int t = min(t0 + tt, t_end - 1);  // rows past the end repeat a valid row; their p is 0
+        dma16(row_addr(row_of(t)) + col * 2, dst + k * 1024);
+      }
+    }
+  };
+
+  // Q^T operand of this wave's k-steps: lane holds features 16*kk + 8*half .. +7 of its head.
   uint4 qf[C::KSTEPS];
   {
     const uint16_t* ql = static_cast<const uint16_t*>(a.q_lat) + (static_cast<int64_t>(b) * a.heads + head) * d_c + s * W;
     const uint16_t* qr = static_cast<const uint16_t*>(a.q_rope) + (static_cast<int64_t>(b) * a.heads + head) * DR;
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      const int f = 16 * kk + 8 * half;
-      qf[kk] = (f < W) ? *reinterpret_cast<const uint4*>(ql + f) : *reinterpret_cast<const uint4*>(qr + (f - W));
+    for (int k = 0; k < C::KSTEPS; ++k) {
+      const int f = 16 * (kh * C::KSTEPS + k) + 8 * half;
+      qf[k] = (f < W) ? *reinterpret_cast<const uint4*>(ql + f) : *reinterpret_cast<const uint4*>(qr + (f - W));
+    }
+  }
+  // Wait for the query now, before the ring starts: otherwise the compiler's own wait for these
+  // loads would sit inside the tile loop and drain the tile DMA with it.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+#pragma unroll
+  for (int k = 0; k < C::KSTEPS; ++k) asm volatile("" : "+v"(qf[k].x), "+v"(qf[k].y), "+v"(qf[k].z), "+v"(qf[k].w));
+  // Logits are scale*log2(e)*(q.k).  A negative scale is moved into the query (exact bf16 sign
+  // flips), so the factor applied in the softmax, cs, is never negative.
+  const float cs = fabsf(scale_log2);
+  if (scale_log2 < 0.f) {
+#pragma unroll
+    for (int k = 0; k < C::KSTEPS; ++k) {
+      qf[k].x ^= 0x80008000u; qf[k].y ^= 0x80008000u; qf[k].z ^= 0x80008000u; qf[k].w ^= 0x80008000u;
     }
   }
 
-  uint4 stage[C::LOADS];
-  auto load_tile = [&](int t0) {
 #pragma unroll
-    for (int k = 0; k < C::LOADS; ++k) {
-      const int idx = tid + k * C::THREADS;
-      const int tok = idx / C::CPR, ch = idx % C::CPR;
-      const int t = t0 + tok;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < kNT * C::CPR && t < t_end) {
-        const int64_t row = cache_row(a.block_table, b, t, a.page_size, a.max_pages_per_seq);
-        const int64_t col = (ch < C::LAT_CPR) ? static_cast<int64_t>(s) * W + ch * 8 : d_c + (ch - C::LAT_CPR) * 8;
-        v = *reinterpret_cast<const uint4*>(cache + row * D + col);
-      }
-      stage[k] = v;
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int j = 0; j < ST - 1; ++j)
+    if (j < n_tiles) issue(j, j);
+
+  // Per-lane LDS offsets (bytes) of the swizzled operand reads.
+  const int swk = swz(l32);  // K operand: token l32
+  int koff[4];
 #pragma unroll
-    for (int k = 0; k < C::LOADS; ++k) {
-      const int idx = tid + k * C::THREADS;
-      if (idx < kNT * C::CPR) {
-        const int tok = idx / C::CPR, ch = idx % C::CPR;
-        *reinterpret_cast<uint4*>(lds + buf * C::TILE_BYTES + tok * C::ROW_BYTES + ch * 16) = stage[k];
-      }
-    }
-  };
+  for (int m = 0; m < 4; ++m) koff[m] = l32 * C::ROW_BYTES + ((((2 * m) | half) ^ swk) << 4);
+  const int grp = lane >> 4, q = lane & 15;
+  const int vt = 4 * half + (q >> 2);  // V operand: token within a 16-token step (and +8)
+  const int swv = swz(vt);
+  int voff[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) voff[m] = vt * C::ROW_BYTES + (((4 * m + 2 * (grp & 1) + ((q & 3) >> 1)) ^ swv) << 4) + 8 * (q & 1);
 
   floatx16_t o_acc[C::CB];
 #pragma unroll
   for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) o_acc[cb][j] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // Online softmax state of the lane's head, in base-2 logit units.  m_ref is the reference
+  // maximum the exponentials are taken against; it is raised (and O, l rescaled) only when a
+  // logit exceeds it by more than 8, so p stays in (0, 2^8] and the rescale almost never runs.
+  // l holds the lane's partial sum over its half of the tokens.
+  float m_ref = -INFINITY, l_run = 0.f;
+#ifndef TPLA_NPF
+#define TPLA_NPF 6
+#endif
+#ifndef TPLA_NPV
+#define TPLA_NPV 4
+#endif
+#ifndef TPLA_SCHAINS
+#define TPLA_SCHAINS 2
+#endif
+  constexpr int NPF = C::KSTEPS < TPLA_NPF ? C::KSTEPS : TPLA_NPF;      // K fragments read ahead of their MFMA
+  constexpr int NPV = 2 * C::CB < TPLA_NPV ? 2 * C::CB : TPLA_NPV;      // value fragments read ahead of their MFMA
 
-  load_tile(t_begin);
-  store_tile(0);
-  __syncthreads();
-
-  int buf = 0;
-  for (int t0 = t_begin; t0 < t_end; t0 += kNT) {
-    const bool has_next = t0 + kNT < t_end;
-    if (has_next) load_tile(t0 + kNT);
-    const unsigned char* tile = lds + buf * C::TILE_BYTES;
-
-    // S^T = K_tile . Q^T  (lane: head l32, tokens 8*(j/4) + 4*half + j%4)
-    floatx16_t sacc;
+  auto tile_at = [&](int stage) { return lds + stage * C::TILE_BYTES; };
+  auto kread = [&](const unsigned char* tile, int k) {
+    const int kk = kh * C::KSTEPS + k;
+    return *reinterpret_cast<const uint4*>(tile + koff[kk & 3] + ((kk >> 2) << 7));
+  };
+  // Value fragment v = ks * CB + cbl: tokens 16*ks.., value block kh*CB + cbl.
+  auto vread = [&](const unsigned char* tile, int v) {
+    const int ks = v / C::CB, cb = kh * C::CB + v % C::CB;
+    const unsigned char* p0 = tile + 16 * ks * C::ROW_BYTES + voff[cb & 1] + ((cb >> 1) << 7);
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0));
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0 + 8 * C::ROW_BYTES));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // S^T partials of one tile over this wave's k-steps, K fragments NPF steps ahead, even and odd
+  // steps in two independent accumulators (lane: head l32, tokens 8*(j/4) + 4*half + j%4).
+  auto qk = [&](const unsigned char* tile, floatx16_t& sa, floatx16_t& sb) {
+    uint4 kf[NPF];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+    for (int k = 0; k < NPF; ++k) kf[k] = kread(tile, k);
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      const uint4 kv = *reinterpret_cast<const uint4*>(tile + l32 * C::ROW_BYTES + (16 * kk + 8 * half) * 2);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
-                                                     __builtin_bit_cast(bf16x8_t, qf[kk]), sacc, 0, 0, 0);
+    for (int j = 0; j < 16; ++j) { sa[j] = 0.f; sb[j] = 0.f; }
+#pragma unroll
+    for (int k = 0; k < C::KSTEPS; ++k) {
+      const uint4 cur = kf[k % NPF];
+      if (k + NPF < C::KSTEPS) kf[k % NPF] = kread(tile, k + NPF);
+      if ((k & 1) && TPLA_SCHAINS == 2)
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur), __builtin_bit_cast(bf16x8_t, qf[k]), sb, 0, 0, 0);
+      else
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur), __builtin_bit_cast(bf16x8_t, qf[k]), sa, 0, 0, 0);
     }
-
-    // Online softmax in base 2 (log2 e folded into the scale).
-    float x[16];
-    float tmax = -INFINITY;
+  };
+  // Partial-logit exchange of a wave pair (KS = 2), double-buffered by tile parity.
+  auto sx_write = [&](int par, const floatx16_t& v) {
+    float4* dst = reinterpret_cast<float4*>(lds + C::SX_OFF + (par * C::NWAVES + wv) * 4096);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int tok = 8 * (j >> 2) + 4 * half + (j & 3);
-      const float v = (t0 + tok < t_end) ? sacc[j] * scale_log2 : -INFINITY;
-      x[j] = v;
-      tmax = fmaxf(tmax, v);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);  // finite: every tile holds at least one valid token
-    const float alpha = exp2f(m_run - m_new);
-    uint32_t pk[8];
-    float psum = 0.f;
+    for (int j4 = 0; j4 < 4; ++j4) dst[j4 * 64 + lane] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
+  };
+  // Full logits of a tile from its partials; both waves of a pair add the halves in the same
+  // order, so they agree bit for bit.
+  auto logits = [&](const floatx16_t& sa, const floatx16_t& sb, int par, float (&x)[16]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p0 = exp2f(x[2 * i] - m_new), p1 = exp2f(x[2 * i + 1] - m_new);
-      psum += p0 + p1;
-      pk[i] = pack_bf16x2(p0, p1);
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.0f)) {
+    for (int j = 0; j < 16; ++j) x[j] = TPLA_SCHAINS == 2 ? sa[j] + sb[j] : sa[j];
+    if constexpr (KS > 1) {
+      const float4* src = reinterpret_cast<const float4*>(lds + C::SX_OFF + (par * C::NWAVES + (wv ^ 1)) * 4096);
 #pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb)
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float4 v = src[j4 * 64 + lane];
+        const float pv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o_acc[cb][j] *= alpha;
-    }
-
-    // O^T += V_tile^T . P^T.  k-step ks covers tokens 16*ks .. 16*ks+15 in the order the softmax
-    // registers hold them: operand slot 8*half + i <-> token 16*ks + 8*(i/4) + 4*half + i%4.
-    const int grp = lane >> 4, q = lane & 15;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]));
-      const int row0 = 16 * ks + 4 * half + (q >> 2);
-#pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb) {
-        const int col = 32 * cb + 16 * (grp & 1) + 4 * (q & 3);
-        const unsigned char* p0 = tile + row0 * C::ROW_BYTES + col * 2;
-        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0));
-        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0 + 8 * C::ROW_BYTES));
-        const short8_t v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o_acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8), pb, o_acc[cb], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) x[4 * j4 + e] = kh == 0 ? x[4 * j4 + e] + pv[e] : pv[e] + x[4 * j4 + e];
       }
     }
+  };
+  // Online softmax of one tile (branch-free): p = 2^(cs*x - m_ref); returns the rescale factor
+  // alpha of O and l (1 unless m_ref was raised).  Masked logits must be -inf.
+  auto softmax = [&](float (&x)[16], uint32_t (&pk)[8]) {
+    float rmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    rmax = fmaxf(rmax, fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])), fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+    rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over both lane halves
+    const float tmax = rmax * cs;
+    const float m_new = tmax > m_ref + 8.0f ? tmax : m_ref;       // first tile: m_ref = -inf
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);    // exactly 1 when not raised, 0 first
+    m_ref = m_new;
+    const float neg_m = -m_new;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int i2 = 0; i2 < 8; ++i2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2], cs, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2 + 1], cs, neg_m));
+      ps0 += p0;
+      ps1 += p1;
+      pk[i2] = pack_bf16x2(p0, p1);
+    }
+    l_run = __builtin_fmaf(l_run, alpha, ps0 + ps1);
+    return alpha;
+  };
+  // The same for the last tile of a chunk, where only its first `valid` tokens count: masked
+  // tokens are left out of the maximum and weigh exactly 0 (also with a zero scale).
+  auto softmax_masked = [&](float (&x)[16], uint32_t (&pk)[8], int valid) {
+    bool keep[16];
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      keep[j] = 8 * (j >> 2) + 4 * half + (j & 3) < valid;
+      if (keep[j]) rmax = fmaxf(rmax, x[j]);
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+    rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // finite: token 0 is valid
+    const float tmax = rmax * cs;
+    const float m_new = tmax > m_ref + 8.0f ? tmax : m_ref;
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    m_ref = m_new;
+    const float neg_m = -m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int i2 = 0; i2 < 8; ++i2) {
+      const float p0 = keep[2 * i2] ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2], cs, neg_m)) : 0.f;
+      const float p1 = keep[2 * i2 + 1] ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2 + 1], cs, neg_m)) : 0.f;
+      ps += p0 + p1;
+      pk[i2] = pack_bf16x2(p0, p1);
+    }
+    l_run = __builtin_fmaf(l_run, alpha, ps);
+    return alpha;
+  };
+  // O^T += V_tile^T . P^T.  k-step ks covers tokens 16*ks .. 16*ks+15 in the order the softmax
+  // registers hold them: operand slot 8*half + i <-> token 16*ks + 8*(i/4) + 4*half + i%4.
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o_acc[cb][j] *= alpha;
+  };
+  auto pv = [&](const unsigned char* tile, const uint32_t (&pk)[8], short8_t (&vf)[NPV]) {
+    const bf16x8_t pb[2] = {__builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3])),
+                            __builtin_bit_cast(bf16x8_t, make_uint4(pk[4], pk[5], pk[6], pk[7]))};
+#pragma unroll
+    for (int v = 0; v < 2 * C::CB; ++v) {
+      const short8_t cur = vf[v % NPV];
+      if (v + NPV < 2 * C::CB) vf[v % NPV] = vread(tile, v + NPV);
+      o_acc[v % C::CB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur), pb[v / C::CB],
+                                                                 o_acc[v % C::CB], 0, 0, 0);
+    }
+  };
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  // Tile j sits in ring stage j % ST.  Waiting for tile j when `newer` tiles were issued after
+  // it: the loads of those may stay in flight, which the wait can express only for the steady
+  // state count; otherwise it drains everything.
+  auto wait_tile = [&](int newer, auto steady) {
+    constexpr int NS = decltype(steady)::value;
+    if (newer == NS) {
+      if (C::REM != 0 && wv < C::REM)
+        wait_vm_lgkm0<NS * (C::PER_LO + 1)>();
+      else
+        wait_vm_lgkm0<NS * C::PER_LO>();
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+  };
+
+  // Prologue: tiles 0..ST-2 are in flight.  Wait for tile 0, start its logits.
+  wait_tile(min(n_tiles - 1, ST - 2), std::integral_constant<int, ST - 2>{});
+  raw_barrier();
+  floatx16_t sa, sb;
+  qk(tile_at(0), sa, sb);
+  if constexpr (KS > 1) {
+    floatx16_t part;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) part[j] = TPLA_SCHAINS == 2 ? sa[j] + sb[j] : sa[j];
+    sx_write(0, part);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Steady state, tile i with tile i+1 resident: the logits of tile i+1 (MFMA) are interleaved
+  // with the softmax of tile i (VALU), then tile i's value product.  A tile that raises the
+  // reference maximum (other than the first: O is still zero then) leaves the inner loop, so that
+  // the rescale of O -- which needs O out of the accumulation registers -- is outside it.
+  int st_cur = 0, st_next = 1 % ST, st_issue = ST - 1;
+  int i = 0;
+  while (i + 1 < n_tiles) {
+    bool raised = false;
+    float alpha = 1.0f;
+    uint32_t pk[8];
+    for (; i + 1 < n_tiles; ++i) {
+      wait_tile(min(n_tiles - 1, ST + i - 2) - (i + 1), std::integral_constant<int, ST - 3>{});
+      raw_barrier();  // tile i+1 visible; tile i-1's stage free; partial logits of tile i visible
+      if (i + ST - 1 < n_tiles) issue(i + ST - 1, st_issue);
+      st_issue = st_issue + 1 == ST ? 0 : st_issue + 1;
+      __builtin_amdgcn_sched_barrier(0);
+
+      float x[16];
+      logits(sa, sb, i & 1, x);
+      const float m_old = m_ref;
+      qk(tile_at(st_next), sa, sb);
+      alpha = softmax(x, pk);
+      // interleave: NPF K reads up front, then per k-step one MFMA, a few VALU, one K read
+      __builtin_amdgcn_sched_group_barrier(0x100, NPF, 0);
+#pragma unroll
+      for (int k = 0; k < C::KSTEPS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        if (k + NPF < C::KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (KS > 1) {
+        floatx16_t part;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part[j] = TPLA_SCHAINS == 2 ? sa[j] + sb[j] : sa[j];
+        sx_write((i + 1) & 1, part);
+      }
+      if (__any(alpha != 1.0f && m_old != -INFINITY)) {  // wave-uniform, rare
+        raised = true;
+        break;
+      }
+      const unsigned char* tile = tile_at(st_cur);
+      short8_t vf[NPV];
+#pragma unroll
+      for (int v = 0; v < NPV; ++v) vf[v] = vread(tile, v);
+      __builtin_amdgcn_sched_barrier(0);
+      pv(tile, pk, vf);
+      __builtin_amdgcn_sched_barrier(0);
+      st_cur = st_next;
+      st_next = st_next + 1 == ST ? 0 : st_next + 1;
+    }
+    if (!raised) break;
+    // finish tile i after raising the reference maximum
+    rescale(alpha);
+    const unsigned char* tile = tile_at(st_cur);
+    short8_t vf[NPV];
+#pragma unroll
+    for (int v = 0; v < NPV; ++v) vf[v] = vread(tile, v);
+    pv(tile, pk, vf);
+    st_cur = st_next;
+    st_next = st_next + 1 == ST ? 0 : st_next + 1;
+    ++i;
+  }
+
+  // Last tile (possibly partial): mask tokens past the end, then its softmax and value product.
+  {
+    if constexpr (KS > 1) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): partial logits written
+      raw_barrier();
+    }
+    const int i = n_tiles - 1;
+    const int t0 = t_begin + i * kNT;
+    float x[16];
+    logits(sa, sb, i & 1, x);
+    uint32_t pk[8];
+    const float alpha = softmax_masked(x, pk, t_end - t0);
+    if (__any(alpha != 1.0f)) rescale(alpha);
+    const unsigned char* tile = tile_at(st_cur);
+    short8_t vf[NPV];
+#pragma unroll
+    for (int v = 0; v < NPV; ++v) vf[v] = vread(tile, v);
+    pv(tile, pk, vf);
   }
 
   // Chunk result: o = O / l, lse = ln 2 * (m + log2 l); the two lane halves hold disjoint tokens.
@@ -190,35 +522,79 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeLaunch a,
   const int64_t part = ((static_cast<int64_t>(b) * a.num_chunks + c) * a.shard_count + s_local) * a.heads + head;
   float* dst = a.part_o + part * W;
 #pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb)
+  for (int cbl = 0; cbl < C::CB; ++cbl) {
+    const int cb = kh * C::CB + cbl;
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int col = 32 * cb + 8 * j4 + 4 * half;
-      const float4 v = make_float4(o_acc[cb][4 * j4] * inv, o_acc[cb][4 * j4 + 1] * inv, o_acc[cb][4 * j4 + 2] * inv,
-                                   o_acc[cb][4 * j4 + 3] * inv);
+      const float4 v = make_float4(o_acc[cbl][4 * j4] * inv, o_acc[cbl][4 * j4 + 1] * inv, o_acc[cbl][4 * j4 + 2] * inv,
+                                   o_acc[cbl][4 * j4 + 3] * inv);
       *reinterpret_cast<float4*>(dst + col) = v;
     }
-  if (half == 0) a.part_lse[part] = (m_run + log2f(l_tot)) * kLn2;
+  }
+  if (half == 0 && kh == 0) a.part_lse[part] = (m_ref + log2f(l_tot)) * kLn2;
 }
 
-template <int W, int DR, int NW>
+template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
 hipError_t launch_one(const DecodeLaunch& a, hipStream_t stream) {
-  using C = Cfg<W, DR, NW>;
-  auto kern = decode_mfma_kernel<W, DR, NW>;
+  using C = Cfg<W, DR, HB, KS, STQ>;
+  auto kern = decode_mfma_kernel<W, DR, HB, KS, STQ, LAYOUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  const dim3 grid(a.num_chunks, a.batch, a.shard_count * (a.heads / (32 * NW)));
+  const int units = a.num_chunks * a.batch;
+  const int members = a.shard_count * (a.heads / (32 * HB));
+  const int64_t blocks = static_cast<int64_t>((units + 7) / 8) * 8 * members;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  int page_shift = -1;
+  if (LAYOUT != 0 && (a.page_size & (a.page_size - 1)) == 0) page_shift = __builtin_ctz(a.page_size);
   const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
-  hipLaunchKernelGGL(kern, grid, dim3(C::THREADS), C::LDS_BYTES, stream, a, scale_log2);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(C::THREADS), C::LDS_BYTES, stream, a, scale_log2,
+                     units, members, page_shift);
   return hipGetLastError();
 }
 
-template <int W, int DR>
+template <int W, int DR, int HB, int KS, int STQ>
+hipError_t launch_layout(const DecodeLaunch& a, hipStream_t stream) {
+  if (a.block_table == nullptr) return launch_one<W, DR, HB, KS, STQ, 0>(a, stream);
+  if (a.page_size % kNT == 0) return launch_one<W, DR, HB, KS, STQ, 1>(a, stream);
+  return launch_one<W, DR, HB, KS, STQ, 2>(a, stream);
+}
+
+// Tile configuration per value width: (largest head-block count per workgroup, key split, ring
+// stages).  Overridable at build time for tuning sweeps.
+#ifndef TPLA_W128_CFG
+#define TPLA_W128_CFG 4, 1, 6
+#endif
+#ifndef TPLA_W256_CFG
+#define TPLA_W256_CFG 4, 1, 6
+#endif
+#ifndef TPLA_W512_CFG
+#define TPLA_W512_CFG 2, 2, 3
+#endif
+struct TileCfg {
+  int hb_max, ks, st;
+};
+constexpr TileCfg kW128{TPLA_W128_CFG}, kW256{TPLA_W256_CFG}, kW512{TPLA_W512_CFG};
+
+constexpr TileCfg tile_cfg(int w) { return w == 128 ? kW128 : (w == 256 ? kW256 : kW512); }
+
+// Head blocks of 32 per workgroup: the largest of (hb_max, 2, 1) that divides the heads.
+int pick_hb(int w, int heads) {
+  const int cap = tile_cfg(w).hb_max;
+  if (cap >= 4 && heads % 128 == 0) return 4;
+  if (cap >= 2 && heads % 64 == 0) return 2;
+  return 1;
+}
+
+template <int W, int HBMAX, int KS, int ST>
 hipError_t launch_w(const DecodeLaunch& a, hipStream_t stream) {
-  if (a.heads % 128 == 0) return launch_one<W, DR, 4>(a, stream);
-  if (a.heads % 64 == 0) return launch_one<W, DR, 2>(a, stream);
-  return launch_one<W, DR, 1>(a, stream);
+  const int hb = pick_hb(W, a.heads);
+  if constexpr (HBMAX >= 4)
+    if (hb == 4) return launch_layout<W, 64, 4, KS, ST>(a, stream);
+  if constexpr (HBMAX >= 2)
+    if (hb == 2) return launch_layout<W, 64, 2, KS, ST>(a, stream);
+  return launch_layout<W, 64, 1, KS, ST>(a, stream);
 }
 
 }  // namespace
@@ -227,12 +603,25 @@ bool mfma_supported(int w, int d_rope, int heads) {
   return (w == 128 || w == 256 || w == 512) && d_rope == 64 && heads % 32 == 0;
 }
 
+void mfma_plan_info(int w, int heads, int* head_groups, int* wgs_per_cu) {
+  const int hb = pick_hb(w, heads);
+  *head_groups = heads / (32 * hb);
+  // one wave per SIMD (the kernels use more than half the register file), so a CU holds
+  // 4 / (waves per workgroup) workgroups
+  const int waves = hb * tile_cfg(w).ks;
+  *wgs_per_cu = waves >= 4 ? 1 : 4 / waves;
+}
+
+int mfma_max_chunk_pages() { return kMaxPages - 2; }
+
 hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t stream) {
   if (!mfma_supported(a.w, a.d_rope, a.heads)) return hipErrorInvalidValue;
+  // the chunk's block-table entries must fit the LDS page list
+  if (a.block_table != nullptr && a.chunk_tokens / a.page_size + 2 > kMaxPages) return hipErrorInvalidValue;
   switch (a.w) {
-    case 128: return launch_w<128, 64>(a, stream);
-    case 256: return launch_w<256, 64>(a, stream);
-    default: return launch_w<512, 64>(a, stream);
+    case 128: return launch_w<128, kW128.hb_max, kW128.ks, kW128.st>(a, stream);
+    case 256: return launch_w<256, kW256.hb_max, kW256.ks, kW256.st>(a, stream);
+    default: return launch_w<512, kW512.hb_max, kW512.ks, kW512.st>(a, stream);
   }
 }
 

@@ -44,6 +44,10 @@ hipError_t launch_decode_generic(const DecodeLaunch& a, int dtype, hipStream_t s
 // Returns hipErrorInvalidValue when no MFMA tile covers the shape (checked by mfma_supported first).
 bool mfma_supported(int w, int d_rope, int heads);
 hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t stream);
+// Workgroups the MFMA kernel runs per (sequence, chunk, shard), and how many fit on one CU.
+void mfma_plan_info(int w, int heads, int* head_groups, int* wgs_per_cu);
+// Largest number of cache pages one chunk of the MFMA kernel may span.
+int mfma_max_chunk_pages();
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 // Rotate q_lat [B*H, d_c] by the Hadamard matrix into dst (fp32 if dst_f32, else bf16).
 hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_latent, void* dst, int dst_f32,

@@ -37,6 +37,9 @@ SMALL = [
                                       transform="wht", paged=True, page_size=8), {}),
     ("f32_g2_wht_paged", dict(batch=2, heads=4, d_latent=64, d_rope=16, shards=2, lens=[200, 17], dtype="f32",
                               transform="wht", paged=True, page_size=16), {}),
+    ("zero_scale_uniform_weights", dict(batch=2, heads=128, shards=2, lens=[100, 33], scale=0.0), {}),
+    ("negative_scale", dict(batch=2, heads=64, shards=4, lens=[250, 64], scale=-0.1), {}),
+    ("single_tile_and_one_token", dict(batch=3, heads=128, shards=1, lens=[32, 1, 31]), {}),
 ]
 
 
