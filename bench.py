@@ -54,7 +54,23 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--chunk-tokens", type=int, default=0)
     p.add_argument("--no-flush", action="store_true", help="do not evict the last-level cache between steps")
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy three times (to scale HBM byte counters)")
     return p.parse_args()
+
+
+def calibration_copy():
+    """A plain copy of known size: each launch reads and writes exactly 1 GiB, so the byte
+    counters a profiler reports for it give the scale factor of those counters."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_read": n, "calibration_copy_bytes_written": n, "launches": 3}))
 
 
 class Workload:
@@ -214,6 +230,9 @@ def main():
                           "n_gpus": args.gpus}))
         log("bench.py measures the single-GPU hot path; multi-GPU runs are not part of this build")
         sys.exit(2)
+    if args.calibration_copy:
+        calibration_copy()
+        return
     import torch
 
     from mla_latent_kv_13_amd import binding
