@@ -24,10 +24,13 @@
 // at LDS base + 16*i, so a tile is laid out in 1 KiB pieces, one per wave instruction.
 //
 // LDS tile layout: token-major rows of KW bf16 (KW = W + D_R) in 16-byte chunks; chunk c of token t
-// sits at position c ^ f(t), f(t) = 2*(t%4) + (t/4)%2 (a permutation within each group of 8
-// chunks).  Eight consecutive tokens reading the same chunk (the K operand) then hit eight
-// different 16-byte bank groups, and so do four consecutive tokens reading two adjacent chunks
-// (the transposed V operand).
+// sits at position c ^ f(t), f(t) = 4*((t/2)%2) + (t/4)%4 (a permutation within each group of 8
+// chunks, period 16 in t).  LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, all 64
+// banks) per cycle and an 8-byte read 32 lanes per cycle.  A row is 128 bytes modulo 256 for
+// every supported width, so the 16 tokens of a K-operand read group (same chunk) land on 16
+// distinct 16-byte bank groups exactly when f is one-to-one on the even and on the odd tokens of
+// each 16; the transposed V read (4 tokens x 4 adjacent chunks per 32 lanes) needs bit 2 of f to
+// differ between tokens t and t+2.
 //
 // Cache layouts: LAYOUT 0 = contiguous (sequence b owns rows b*page_size...), 1 = paged with
 // page_size a multiple of 32 (a tile never straddles a page), 2 = any other paging.  In layouts
@@ -76,7 +79,7 @@ struct Cfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7
 // meaning no wait, lgkmcnt [11:8] = 0).
@@ -251,11 +254,13 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
 #pragma unroll
   for (int m = 0; m < 4; ++m) koff[m] = l32 * C::ROW_BYTES + ((((2 * m) | half) ^ swk) << 4);
   const int grp = lane >> 4, q = lane & 15;
-  const int vt = 4 * half + (q >> 2);  // V operand: token within a 16-token step (and +8)
-  const int swv = swz(vt);
-  int voff[2];
+  const int vt = 4 * half + (q >> 2);  // V operand: token vt (low read) and vt + 8 (high read) of a 16-token step
+  int voff[2][2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) voff[m] = vt * C::ROW_BYTES + (((4 * m + 2 * (grp & 1) + ((q & 3) >> 1)) ^ swv) << 4) + 8 * (q & 1);
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      voff[hi][m] = (vt + 8 * hi) * C::ROW_BYTES + (((4 * m + 2 * (grp & 1) + ((q & 3) >> 1)) ^ swz(vt + 8 * hi)) << 4) + 8 * (q & 1);
 
   floatx16_t o_acc[C::CB];
 #pragma unroll
@@ -268,139 +273,96 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
   // l holds the lane's partial sum over its half of the tokens.
   float m_ref = -INFINITY, l_run = 0.f;
 #ifndef TPLA_NPF
-#define TPLA_NPF 6
+#define TPLA_NPF 4
 #endif
 #ifndef TPLA_NPV
 #define TPLA_NPV 4
 #endif
-#ifndef TPLA_SCHAINS
-#define TPLA_SCHAINS 2
-#endif
-  constexpr int NPF = C::KSTEPS < TPLA_NPF ? C::KSTEPS : TPLA_NPF;      // K fragments read ahead of their MFMA
-  constexpr int NPV = 2 * C::CB < TPLA_NPV ? 2 * C::CB : TPLA_NPV;      // value fragments read ahead of their MFMA
+  constexpr int KST = C::KSTEPS;
+  constexpr int NV = 2 * C::CB;                       // value fragments (MFMAs) per tile
+  constexpr int NPF = KST < TPLA_NPF ? KST : TPLA_NPF;  // K fragments read ahead of their MFMA
+  constexpr int NPV = NV < TPLA_NPV ? NV : TPLA_NPV;    // value fragments read ahead of their MFMA
+  static_assert(NPV <= KST, "value prefetch rides on the k-steps of the next tile's logits");
 
   auto tile_at = [&](int stage) { return lds + stage * C::TILE_BYTES; };
   auto kread = [&](const unsigned char* tile, int k) {
-    const int kk = kh * C::KSTEPS + k;
+    const int kk = kh * KST + k;
     return *reinterpret_cast<const uint4*>(tile + koff[kk & 3] + ((kk >> 2) << 7));
   };
   // Value fragment v = ks * CB + cbl: tokens 16*ks.., value block kh*CB + cbl.
   auto vread = [&](const unsigned char* tile, int v) {
     const int ks = v / C::CB, cb = kh * C::CB + v % C::CB;
-    const unsigned char* p0 = tile + 16 * ks * C::ROW_BYTES + voff[cb & 1] + ((cb >> 1) << 7);
-    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0));
-    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0 + 8 * C::ROW_BYTES));
+    const unsigned char* p0 = tile + 16 * ks * C::ROW_BYTES + ((cb >> 1) << 7);
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0 + voff[0][cb & 1]));
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p0 + voff[1][cb & 1]));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  // S^T partials of one tile over this wave's k-steps, K fragments NPF steps ahead, even and odd
-  // steps in two independent accumulators (lane: head l32, tokens 8*(j/4) + 4*half + j%4).
-  auto qk = [&](const unsigned char* tile, floatx16_t& sa, floatx16_t& sb) {
-    uint4 kf[NPF];
-#pragma unroll
-    for (int k = 0; k < NPF; ++k) kf[k] = kread(tile, k);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) { sa[j] = 0.f; sb[j] = 0.f; }
-#pragma unroll
-    for (int k = 0; k < C::KSTEPS; ++k) {
-      const uint4 cur = kf[k % NPF];
-      if (k + NPF < C::KSTEPS) kf[k % NPF] = kread(tile, k + NPF);
-      if ((k & 1) && TPLA_SCHAINS == 2)
-        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur), __builtin_bit_cast(bf16x8_t, qf[k]), sb, 0, 0, 0);
-      else
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur), __builtin_bit_cast(bf16x8_t, qf[k]), sa, 0, 0, 0);
-    }
+  auto mfma = [](const auto& a_op, const auto& b_op, const floatx16_t& c_acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a_op), __builtin_bit_cast(bf16x8_t, b_op),
+                                                   c_acc, 0, 0, 0);
   };
-  // Partial-logit exchange of a wave pair (KS = 2), double-buffered by tile parity.
+  // Partial logits of a wave pair (KS = 2), double-buffered by tile parity.
   auto sx_write = [&](int par, const floatx16_t& v) {
     float4* dst = reinterpret_cast<float4*>(lds + C::SX_OFF + (par * C::NWAVES + wv) * 4096);
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) dst[j4 * 64 + lane] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
   };
-  // Full logits of a tile from its partials; both waves of a pair add the halves in the same
-  // order, so they agree bit for bit.
-  auto logits = [&](const floatx16_t& sa, const floatx16_t& sb, int par, float (&x)[16]) {
+  auto sx_read = [&](int par, float4 (&pv)[4]) {
+    const float4* src = reinterpret_cast<const float4*>(lds + C::SX_OFF + (par * C::NWAVES + (wv ^ 1)) * 4096);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = TPLA_SCHAINS == 2 ? sa[j] + sb[j] : sa[j];
-    if constexpr (KS > 1) {
-      const float4* src = reinterpret_cast<const float4*>(lds + C::SX_OFF + (par * C::NWAVES + (wv ^ 1)) * 4096);
+    for (int j4 = 0; j4 < 4; ++j4) pv[j4] = src[j4 * 64 + lane];
+  };
+  // Full logits of a tile from this wave's partial and (KS = 2) the partner's; both waves of a
+  // pair add the halves in the same order, so they agree bit for bit.
+  auto logits = [&](const floatx16_t& sv, const float4 (&pv)[4], float (&x)[16]) {
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const float4 v = src[j4 * 64 + lane];
-        const float pv[4] = {v.x, v.y, v.z, v.w};
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const float o4[4] = {pv[j4].x, pv[j4].y, pv[j4].z, pv[j4].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * j4 + e] = kh == 0 ? x[4 * j4 + e] + pv[e] : pv[e] + x[4 * j4 + e];
+      for (int e = 0; e < 4; ++e) {
+        const float own = sv[4 * j4 + e];
+        x[4 * j4 + e] = KS == 1 ? own : (kh == 0 ? own + o4[e] : o4[e] + own);
       }
     }
   };
-  // Online softmax of one tile (branch-free): p = 2^(cs*x - m_ref); returns the rescale factor
-  // alpha of O and l (1 unless m_ref was raised).  Masked logits must be -inf.
-  auto softmax = [&](float (&x)[16], uint32_t (&pk)[8]) {
+  // First half of the online softmax of a tile: the new reference maximum (over both lane halves,
+  // i.e. all 32 tokens of the lane's head) and the rescale factor alpha of O and l (exactly 1
+  // unless the reference was raised).  Masked logits must be -inf here.
+  auto softmax_max = [&](const float (&x)[16], float& neg_m) {
     float rmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     rmax = fmaxf(rmax, fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])), fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
-    rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over both lane halves
+    rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     const float tmax = rmax * cs;
-    const float m_new = tmax > m_ref + 8.0f ? tmax : m_ref;       // first tile: m_ref = -inf
-    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);    // exactly 1 when not raised, 0 first
+    const float m_new = tmax > m_ref + 8.0f ? tmax : m_ref;      // first tile: m_ref = -inf
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // exactly 1 when not raised, 0 first
     m_ref = m_new;
-    const float neg_m = -m_new;
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int i2 = 0; i2 < 8; ++i2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2], cs, neg_m));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2 + 1], cs, neg_m));
-      ps0 += p0;
-      ps1 += p1;
-      pk[i2] = pack_bf16x2(p0, p1);
-    }
-    l_run = __builtin_fmaf(l_run, alpha, ps0 + ps1);
+    neg_m = -m_new;
     return alpha;
   };
-  // The same for the last tile of a chunk, where only its first `valid` tokens count: masked
-  // tokens are left out of the maximum and weigh exactly 0 (also with a zero scale).
-  auto softmax_masked = [&](float (&x)[16], uint32_t (&pk)[8], int valid) {
-    bool keep[16];
-    float rmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      keep[j] = 8 * (j >> 2) + 4 * half + (j & 3) < valid;
-      if (keep[j]) rmax = fmaxf(rmax, x[j]);
-    }
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
-    rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // finite: token 0 is valid
-    const float tmax = rmax * cs;
-    const float m_new = tmax > m_ref + 8.0f ? tmax : m_ref;
-    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-    m_ref = m_new;
-    const float neg_m = -m_new;
-    float ps = 0.f;
-#pragma unroll
-    for (int i2 = 0; i2 < 8; ++i2) {
-      const float p0 = keep[2 * i2] ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2], cs, neg_m)) : 0.f;
-      const float p1 = keep[2 * i2 + 1] ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2 + 1], cs, neg_m)) : 0.f;
-      ps += p0 + p1;
-      pk[i2] = pack_bf16x2(p0, p1);
-    }
-    l_run = __builtin_fmaf(l_run, alpha, ps);
-    return alpha;
+  // Second half, one pair of logits: p = 2^(cs*x - m_ref), packed to bf16 for the value product.
+  auto softmax_pair = [&](const float (&x)[16], int j, float neg_m, uint32_t (&pk)[8], float& ps) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m));
+    ps += p0 + p1;
+    pk[j] = pack_bf16x2(p0, p1);
   };
-  // O^T += V_tile^T . P^T.  k-step ks covers tokens 16*ks .. 16*ks+15 in the order the softmax
-  // registers hold them: operand slot 8*half + i <-> token 16*ks + 8*(i/4) + 4*half + i%4.
   auto rescale = [&](float alpha) {
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) o_acc[cb][j] *= alpha;
   };
+  // O^T += V_tile^T . P^T.  k-step ks covers tokens 16*ks .. 16*ks+15 in the order the softmax
+  // registers hold them: operand slot 8*half + i <-> token 16*ks + 8*(i/4) + 4*half + i%4.
+  // The first NPV value fragments are already in vf.
   auto pv = [&](const unsigned char* tile, const uint32_t (&pk)[8], short8_t (&vf)[NPV]) {
-    const bf16x8_t pb[2] = {__builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3])),
-                            __builtin_bit_cast(bf16x8_t, make_uint4(pk[4], pk[5], pk[6], pk[7]))};
+    const uint4 pb[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
 #pragma unroll
-    for (int v = 0; v < 2 * C::CB; ++v) {
-      const short8_t cur = vf[v % NPV];
-      if (v + NPV < 2 * C::CB) vf[v % NPV] = vread(tile, v + NPV);
-      o_acc[v % C::CB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur), pb[v / C::CB],
-                                                                 o_acc[v % C::CB], 0, 0, 0);
+    for (int v = 0; v < NV; ++v) {
+      o_acc[v % C::CB] = mfma(vf[v % NPV], pb[v / C::CB], o_acc[v % C::CB]);
+      if (v + NPV < NV) vf[v % NPV] = vread(tile, v + NPV);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -419,78 +381,98 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
     }
   };
 
-  // Prologue: tiles 0..ST-2 are in flight.  Wait for tile 0, start its logits.
+  // Prologue: tiles 0..ST-2 are in flight.  Wait for tile 0 and compute its logits.
   wait_tile(min(n_tiles - 1, ST - 2), std::integral_constant<int, ST - 2>{});
   raw_barrier();
-  floatx16_t sa, sb;
-  qk(tile_at(0), sa, sb);
-  if constexpr (KS > 1) {
-    floatx16_t part;
+  floatx16_t s_cur;
+  {
+    const unsigned char* t0 = tile_at(0);
+    uint4 kf[NPF];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) part[j] = TPLA_SCHAINS == 2 ? sa[j] + sb[j] : sa[j];
-    sx_write(0, part);
+    for (int k = 0; k < NPF; ++k) kf[k] = kread(t0, k);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s_cur[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KST; ++k) {
+      s_cur = mfma(kf[k % NPF], qf[k], s_cur);
+      if (k + NPF < KST) kf[k % NPF] = kread(t0, k + NPF);
+    }
+    if constexpr (KS > 1) sx_write(0, s_cur);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // Steady state, tile i with tile i+1 resident: the logits of tile i+1 (MFMA) are interleaved
-  // with the softmax of tile i (VALU), then tile i's value product.  A tile that raises the
-  // reference maximum (other than the first: O is still zero then) leaves the inner loop, so that
-  // the rescale of O -- which needs O out of the accumulation registers -- is outside it.
+  // Steady state, tile i with tile i+1 resident.  Each k-step of the logits of tile i+1 (one
+  // MFMA) also carries one read-ahead K fragment, up to one pair of tile i's softmax and, in the
+  // last NPV steps, one value fragment of tile i; then comes tile i's value product, each MFMA
+  // with one read-ahead value fragment.  The steps are fenced so that the compiler keeps this
+  // order, which hides the LDS latency behind the matrix cores and the softmax arithmetic in the
+  // gaps between MFMA issues.
+  // A tile that raises the reference maximum (other than the first: O is still zero then) leaves
+  // the inner loop before its value product, so that the rescale of O -- which needs O out of the
+  // accumulation registers -- stays outside the steady-state loop.
   int st_cur = 0, st_next = 1 % ST, st_issue = ST - 1;
   int i = 0;
+  floatx16_t s_nxt;
+  uint32_t pk[8];
+  float alpha = 1.0f;
   while (i + 1 < n_tiles) {
     bool raised = false;
-    float alpha = 1.0f;
-    uint32_t pk[8];
     for (; i + 1 < n_tiles; ++i) {
       wait_tile(min(n_tiles - 1, ST + i - 2) - (i + 1), std::integral_constant<int, ST - 3>{});
       raw_barrier();  // tile i+1 visible; tile i-1's stage free; partial logits of tile i visible
       if (i + ST - 1 < n_tiles) issue(i + ST - 1, st_issue);
       st_issue = st_issue + 1 == ST ? 0 : st_issue + 1;
+      const unsigned char* tn = tile_at(st_next);
+      const unsigned char* tc = tile_at(st_cur);
+      uint4 kf[NPF];
+#pragma unroll
+      for (int k = 0; k < NPF; ++k) kf[k] = kread(tn, k);
+      float4 pvx[4];
+      if constexpr (KS > 1) sx_read(i & 1, pvx);
       __builtin_amdgcn_sched_barrier(0);
 
       float x[16];
-      logits(sa, sb, i & 1, x);
+      logits(s_cur, pvx, x);
       const float m_old = m_ref;
-      qk(tile_at(st_next), sa, sb);
-      alpha = softmax(x, pk);
-      // interleave: NPF K reads up front, then per k-step one MFMA, a few VALU, one K read
-      __builtin_amdgcn_sched_group_barrier(0x100, NPF, 0);
-#pragma unroll
-      for (int k = 0; k < C::KSTEPS; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        if (k + NPF < C::KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      float neg_m;
+      alpha = softmax_max(x, neg_m);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (KS > 1) {
-        floatx16_t part;
+
 #pragma unroll
-        for (int j = 0; j < 16; ++j) part[j] = TPLA_SCHAINS == 2 ? sa[j] + sb[j] : sa[j];
-        sx_write((i + 1) & 1, part);
+      for (int j = 0; j < 16; ++j) s_nxt[j] = 0.f;
+      float ps = 0.f;
+      short8_t vf[NPV];
+#pragma unroll
+      for (int k = 0; k < KST; ++k) {
+        s_nxt = mfma(kf[k % NPF], qf[k], s_nxt);
+        if (k + NPF < KST) kf[k % NPF] = kread(tn, k + NPF);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if ((j * KST) / 8 == k) softmax_pair(x, j, neg_m, pk, ps);
+        if (k >= KST - NPV) vf[k - (KST - NPV)] = vread(tc, k - (KST - NPV));
+        __builtin_amdgcn_sched_barrier(0);
       }
+      l_run = __builtin_fmaf(l_run, alpha, ps);
+      if constexpr (KS > 1) sx_write((i + 1) & 1, s_nxt);
       if (__any(alpha != 1.0f && m_old != -INFINITY)) {  // wave-uniform, rare
         raised = true;
         break;
       }
-      const unsigned char* tile = tile_at(st_cur);
-      short8_t vf[NPV];
-#pragma unroll
-      for (int v = 0; v < NPV; ++v) vf[v] = vread(tile, v);
       __builtin_amdgcn_sched_barrier(0);
-      pv(tile, pk, vf);
-      __builtin_amdgcn_sched_barrier(0);
+      pv(tc, pk, vf);
+      s_cur = s_nxt;
       st_cur = st_next;
       st_next = st_next + 1 == ST ? 0 : st_next + 1;
     }
     if (!raised) break;
     // finish tile i after raising the reference maximum
     rescale(alpha);
-    const unsigned char* tile = tile_at(st_cur);
+    const unsigned char* tc = tile_at(st_cur);
     short8_t vf[NPV];
 #pragma unroll
-    for (int v = 0; v < NPV; ++v) vf[v] = vread(tile, v);
-    pv(tile, pk, vf);
+    for (int v = 0; v < NPV; ++v) vf[v] = vread(tc, v);
+    pv(tc, pk, vf);
+    s_cur = s_nxt;
     st_cur = st_next;
     st_next = st_next + 1 == ST ? 0 : st_next + 1;
     ++i;
@@ -498,16 +480,34 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
 
   // Last tile (possibly partial): mask tokens past the end, then its softmax and value product.
   {
-    if constexpr (KS > 1) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): partial logits written
-      raw_barrier();
-    }
     const int i = n_tiles - 1;
-    const int t0 = t_begin + i * kNT;
+    float4 pvx[4];
+    if constexpr (KS > 1) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own partial logits written
+      raw_barrier();
+      sx_read(i & 1, pvx);
+    }
+    const int valid = t_end - (t_begin + i * kNT);
     float x[16];
-    logits(sa, sb, i & 1, x);
+    logits(s_cur, pvx, x);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (8 * (j >> 2) + 4 * half + (j & 3) >= valid) x[j] = -INFINITY;  // token 0 is always valid
+    float neg_m;
+    const float alpha = softmax_max(x, neg_m);
     uint32_t pk[8];
-    const float alpha = softmax_masked(x, pk, t_end - t0);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool k0 = 8 * ((2 * j) >> 2) + 4 * half + ((2 * j) & 3) < valid;
+      const bool k1 = 8 * ((2 * j + 1) >> 2) + 4 * half + ((2 * j + 1) & 3) < valid;
+      // masked tokens weigh exactly 0, also when the scale is zero
+      const float p0 = k0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m)) : 0.f;
+      const float p1 = k1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m)) : 0.f;
+      ps += p0 + p1;
+      pk[j] = pack_bf16x2(p0, p1);
+    }
+    l_run = __builtin_fmaf(l_run, alpha, ps);
     if (__any(alpha != 1.0f)) rescale(alpha);
     const unsigned char* tile = tile_at(st_cur);
     short8_t vf[NPV];
