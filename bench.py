@@ -4,10 +4,11 @@
 One step = one decode call through the C ABI over one batch of the workload (the
 query rotation when the cache is Hadamard-rotated, the split-K decode kernel and the
 log-sum-exp merge / shard sum), with the cache, block table and queries resident in
-HBM.  Before every step, timed or not, a 1 GiB buffer is overwritten so that no
-part of the cache survives in the 256 MB last-level cache: the figures are HBM
-figures.  Steps are timed with HIP events on the call's stream; the split-K decode
-kernel is also timed alone with events the library records around it.
+HBM.  Before every step, timed or not, a 1 GiB buffer is read so that no part of
+the cache survives in the 256 MB last-level cache: the figures are HBM figures.
+Steps are timed with HIP events on the call's stream around the whole call; the
+split-K decode kernel is then timed alone, over as many further steps, with events
+the library records around it on the same stream.
 
 Cache eviction reads a 1 GiB buffer (a reduction with a scalar result): reading leaves only
 clean lines behind, whereas overwriting a buffer would leave up to 256 MB of dirty lines whose
@@ -140,6 +141,9 @@ class Workload:
 
 
 def time_workload(w: Workload, steps: int, warmup: int, flush: bool):
+    """Time `steps` whole calls (events around the call only), then the split-K decode kernel
+    alone in `steps` further calls (events the library records around that kernel).  Event
+    markers inside a call cost it several microseconds, so the two are measured apart."""
     import torch
 
     flush_buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda:0") if flush else None
@@ -152,18 +156,26 @@ def time_workload(w: Workload, steps: int, warmup: int, flush: bool):
         evict()
         w.call()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev + kev:  # materialise the events outside the timed steps
+        e[0].record()
+        e[1].record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         evict()
         ev[i][0].record()
-        w.call(events=(ev[i][1], ev[i][2]))
-        ev[i][3].record()
+        w.call()
+        ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = [e[0].elapsed_time(e[3]) for e in ev]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    for i in range(steps):
+        evict()
+        w.call(events=(kev[i][0], kev[i][1]))
+    torch.cuda.synchronize()
+    call_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[0].elapsed_time(e[1]) for e in kev]
     mean_call = statistics.fmean(call_ms)
     mean_dec = statistics.fmean(dec_ms)
     return {

@@ -40,6 +40,7 @@ SMALL = [
     ("zero_scale_uniform_weights", dict(batch=2, heads=128, shards=2, lens=[100, 33], scale=0.0), {}),
     ("negative_scale", dict(batch=2, heads=64, shards=4, lens=[250, 64], scale=-0.1), {}),
     ("single_tile_and_one_token", dict(batch=3, heads=128, shards=1, lens=[32, 1, 31]), {}),
+    ("more_than_64_chunks", dict(batch=2, heads=32, shards=2, lens=[5000, 4100]), dict(chunk_tokens=64)),
 ]
 
 
