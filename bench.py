@@ -204,7 +204,7 @@ def traffic_for_current_kernel(workload_name: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(c, budget_s: float = 20.0):
+def cpu_baseline(c, budget_s: float = 15.0):
     """The fp64 oracle on the host cores, on whole sequences of the headline workload, repeated
     over the batch until about budget_s of work (decode computation only)."""
     import numpy as np
@@ -220,7 +220,7 @@ def cpu_baseline(c, budget_s: float = 20.0):
     q_rope = inputs.stored_to_f64(c.q_rope, c.dtype)
     done_tokens, spent, seqs = 0, 0.0, 0
     b = 0
-    while spent < budget_s and seqs < 4 * c.batch:
+    while spent < budget_s:
         t0 = time.perf_counter()
         oracle.tpla_decode_sharded(pool[b:b + 1], None if c.block_table is None else c.block_table[b:b + 1],
                                    c.seq_lens[b:b + 1], q_lat[b:b + 1], q_rope[b:b + 1], c.scale, c.shards,

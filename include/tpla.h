@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TPLA_ABI_VERSION 1
+#define TPLA_ABI_VERSION 2
 
 typedef enum {
   TPLA_OK = 0,
@@ -98,12 +98,20 @@ typedef struct {
  *   has no MFMA tile).
  * decode_begin, decode_end: hipEvent_t handles (as void*) recorded on the
  *   call's stream immediately before and after the split-K decode kernel, or
- *   NULL; they time that kernel alone. */
+ *   NULL; they time that kernel alone.
+ * schedule: how the MFMA kernel shares the batch's work out: 0 = library
+ *   choice (balanced for a paged cache, chunked otherwise); 1 = chunked (fixed
+ *   chunks of chunk_tokens per sequence); 2 = balanced (each workgroup takes an
+ *   equal share of all 32-token tiles of the batch, across sequence
+ *   boundaries, so that ragged lengths load the GPU evenly; chunk_tokens is
+ *   then ignored).  The generic kernel always uses chunks.  Both schedules give
+ *   the same result up to floating-point rounding of the merge. */
 typedef struct {
   int32_t chunk_tokens;
   int32_t kernel;
   void* decode_begin;
   void* decode_end;
+  int32_t schedule;
 } tpla_decode_opts_t;
 
 int32_t     tpla_abi_version(void);

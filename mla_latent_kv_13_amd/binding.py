@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "TPLA_OK", 1: "TPLA_ERR_INVALID_ARGUMENT", 2: "TPLA_ERR_UNSUP
 DTYPES = {"f32": 0, "bf16": 1}
 TRANSFORMS = {"identity": 0, "wht": 1}
 KERNELS = {"auto": 0, "generic": 1, "mfma": 2}
+SCHEDULES = {"auto": 0, "chunked": 1, "balanced": 2}
 
 EXPORTED = ["tpla_abi_version", "tpla_status_string", "tpla_last_error", "tpla_workspace_size",
             "latent_cache_append", "tpla_decode_sharded", "tpla_decode_sharded_ex", "mla_decode_absorbed"]
@@ -42,7 +43,7 @@ class CacheDesc(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("chunk_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("decode_begin", ctypes.c_void_p), ("decode_end", ctypes.c_void_p)]
+                ("decode_begin", ctypes.c_void_p), ("decode_end", ctypes.c_void_p), ("schedule", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -128,11 +129,12 @@ def _event_handle(ev):
     return ctypes.c_void_p(ev.cuda_event)
 
 
-def _opts(chunk_tokens: int = 0, kernel: str = "auto", events=None):
-    if not chunk_tokens and kernel == "auto" and events is None:
+def _opts(chunk_tokens: int = 0, kernel: str = "auto", events=None, schedule: str = "auto"):
+    if not chunk_tokens and kernel == "auto" and events is None and schedule == "auto":
         return None
     begin, end = events if events is not None else (None, None)
-    return ctypes.byref(DecodeOpts(int(chunk_tokens), KERNELS[kernel], _event_handle(begin), _event_handle(end)))
+    return ctypes.byref(DecodeOpts(int(chunk_tokens), KERNELS[kernel], _event_handle(begin), _event_handle(end),
+                                   SCHEDULES[schedule]))
 
 
 def abi_version() -> int:
@@ -140,12 +142,12 @@ def abi_version() -> int:
 
 
 def workspace_size(desc: Desc, batch: int, heads: int, num_shards: int, shard_count: int, max_seq_len: int,
-                   chunk_tokens: int = 0, kernel: str = "auto") -> int:
+                   chunk_tokens: int = 0, kernel: str = "auto", schedule: str = "auto") -> int:
     lib = load_library()
     out = ctypes.c_size_t(0)
     cdesc = desc.c()
     _check(lib.tpla_workspace_size(ctypes.byref(cdesc), batch, heads, num_shards, shard_count, max_seq_len,
-                                   _opts(chunk_tokens, kernel), ctypes.byref(out)))
+                                   _opts(chunk_tokens, kernel, None, schedule), ctypes.byref(out)))
     return int(out.value)
 
 
@@ -170,7 +172,7 @@ def tpla_decode_sharded(desc: Desc, cache: torch.Tensor, block_table: torch.Tens
                         max_seq_len: int, shard_begin: int = 0, shard_count: int | None = None,
                         out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, want_lse: bool = True,
-                        chunk_tokens: int = 0, kernel: str = "auto", events=None, stream=None):
+                        chunk_tokens: int = 0, kernel: str = "auto", events=None, stream=None, schedule: str = "auto"):
     """TPLA decode; returns (out [B, H, d_latent] fp32, lse [B, shard_count, H] fp32 or None).
 
     ``events=(begin, end)`` (torch.cuda.Event with timing) are recorded around the split-K
@@ -185,7 +187,7 @@ def tpla_decode_sharded(desc: Desc, cache: torch.Tensor, block_table: torch.Tens
         out = torch.empty((batch, heads, desc.d_latent), dtype=torch.float32, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((batch, shard_count, heads), dtype=torch.float32, device=dev)
-    need = workspace_size(desc, batch, heads, num_shards, shard_count, max_seq_len, chunk_tokens, kernel)
+    need = workspace_size(desc, batch, heads, num_shards, shard_count, max_seq_len, chunk_tokens, kernel, schedule)
     if workspace is None:
         workspace = alloc_workspace(need, dev)
     lib = load_library()
@@ -193,7 +195,7 @@ def tpla_decode_sharded(desc: Desc, cache: torch.Tensor, block_table: torch.Tens
     _check(lib.tpla_decode_sharded_ex(ctypes.byref(cdesc), _ptr(cache), _ptr(block_table), _ptr(seq_lens), batch, heads,
                                       max_seq_len, _ptr(q_latent), _ptr(q_rope), ctypes.c_float(scale), num_shards,
                                       shard_begin, shard_count, _ptr(out), _ptr(lse), _ptr(workspace),
-                                      workspace.numel(), _opts(chunk_tokens, kernel, events), _stream(stream)))
+                                      workspace.numel(), _opts(chunk_tokens, kernel, events, schedule), _stream(stream)))
     return out, lse
 
 

@@ -44,7 +44,10 @@ struct Plan {
   int kernel;        // 1 generic, 2 MFMA
   int chunk_tokens;
   int num_chunks;
-  size_t off_qrot, off_part_o, off_part_lse, total;
+  int sched;         // 0 chunked, 1 balanced
+  int workers;       // balanced: workgroups per (shard, head group)
+  int64_t slots;     // partial slots per (shard, head)
+  size_t off_qrot, off_prefix, off_part_o, off_part_lse, total;
 };
 
 int32_t check_desc(const tpla_cache_desc_t* d) {
@@ -102,7 +105,7 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
       const int64_t per_index = static_cast<int64_t>(batch) * shard_count * head_groups;
       const int64_t slots = static_cast<int64_t>(kComputeUnits) * per_cu;
       int64_t per_seq = std::max<int64_t>(1, (slots + per_index - 1) / per_index);
-      if (d->max_pages_per_seq > 0) per_seq = std::max<int64_t>(per_seq, 16);  // ragged lengths: finer chunks balance better
+      if (d->max_pages_per_seq > 0) per_seq = std::max<int64_t>(per_seq, 32);  // ragged lengths: finer chunks balance better
       ct = static_cast<int>(round_up((span + per_seq - 1) / per_seq, 64));
       ct = std::max(ct, 256);
     } else {
@@ -126,6 +129,31 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
   }
   plan->chunk_tokens = ct;
   plan->num_chunks = nc;
+  plan->sched = 0;
+  plan->workers = 0;
+  plan->slots = static_cast<int64_t>(batch) * nc;
+  const int req_sched = opts ? opts->schedule : 0;
+  if (req_sched < 0 || req_sched > 2) return fail(TPLA_ERR_INVALID_ARGUMENT, "opts->schedule must be 0, 1 or 2");
+  const int64_t max_tiles = static_cast<int64_t>(batch) * ((static_cast<int64_t>(span) + 31) / 32);
+  const bool balanced_ok = plan->kernel == 2 && max_tiles < (int64_t(1) << 30);
+  if (req_sched == 2 && !balanced_ok)
+    return fail(TPLA_ERR_UNSUPPORTED, "the balanced schedule needs the MFMA kernel and fewer than 2^30 tiles");
+  if (balanced_ok && (req_sched == 2 || (req_sched == 0 && d->max_pages_per_seq > 0))) {
+    // One workgroup per slot of the chip, and enough of them that no share of tiles spans more
+    // cache pages than a workgroup stages.
+    int head_groups = 1, per_cu = 1;
+    tpla::mfma_plan_info(w, heads, &head_groups, &per_cu);
+    const int64_t members = static_cast<int64_t>(shard_count) * head_groups;
+    int64_t workers = std::max<int64_t>(1, static_cast<int64_t>(kComputeUnits) * per_cu / members);
+    if (d->max_pages_per_seq > 0) {
+      const int64_t cap_tiles = std::max<int64_t>(1, static_cast<int64_t>(tpla::mfma_max_segment_pages() - 1) * d->page_size / 32 - 1);
+      workers = std::max(workers, (max_tiles + cap_tiles - 1) / cap_tiles);
+    }
+    workers = std::min<int64_t>(workers, std::max<int64_t>(1, max_tiles));
+    plan->sched = 1;
+    plan->workers = static_cast<int>(workers);
+    plan->slots = batch + workers;
+  }
 
   size_t off = 0;
   plan->off_qrot = off;
@@ -133,10 +161,12 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
     const size_t elem = plan->kernel == 1 ? 4 : 2;
     off += round_up(static_cast<size_t>(batch) * heads * d->d_latent * elem, 256);
   }
+  plan->off_prefix = off;
+  if (plan->sched == 1) off += round_up(static_cast<size_t>(batch + 1) * 4, 256);
   plan->off_part_o = off;
-  off += round_up(static_cast<size_t>(batch) * nc * shard_count * heads * static_cast<size_t>(w) * 4, 256);
+  off += round_up(static_cast<size_t>(plan->slots) * shard_count * heads * static_cast<size_t>(w) * 4, 256);
   plan->off_part_lse = off;
-  off += round_up(static_cast<size_t>(batch) * nc * shard_count * heads * 4, 256);
+  off += round_up(static_cast<size_t>(plan->slots) * shard_count * heads * 4, 256);
   plan->total = off;
   return TPLA_OK;
 }
@@ -194,8 +224,15 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
   L.num_chunks = plan.num_chunks;
   L.part_o = reinterpret_cast<float*>(ws + plan.off_part_o);
   L.part_lse = reinterpret_cast<float*>(ws + plan.off_part_lse);
+  L.sched = plan.sched;
+  L.workers = plan.workers;
+  L.tile_prefix = reinterpret_cast<const int*>(ws + plan.off_prefix);
 
   hipError_t e;
+  if (plan.sched == 1) {
+    e = tpla::launch_tile_prefix(seq_lens, batch, reinterpret_cast<int*>(ws + plan.off_prefix), stream);
+    if (e != hipSuccess) return hip_fail(e, "tile prefix launch");
+  }
   if (wht) {
     void* qrot = ws + plan.off_qrot;
     const int dst_f32 = plan.kernel == 1 ? 1 : 0;
@@ -231,6 +268,9 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
   M.shard_count = shard_count;
   M.chunk_tokens = plan.chunk_tokens;
   M.num_chunks = plan.num_chunks;
+  M.sched = plan.sched;
+  M.workers = plan.workers;
+  M.tile_prefix = L.tile_prefix;
   M.wht = wht ? 1 : 0;
   M.out = out;
   M.lse = lse;

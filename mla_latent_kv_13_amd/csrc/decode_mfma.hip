@@ -136,14 +136,51 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
   const int member = slot % members;
   const int u = (slot / members) * 8 + xcd;
   if (u >= units) return;
-  const int c = u % a.num_chunks, b = u / a.num_chunks;
   const int groups = a.heads / (32 * HB);
   const int s_local = member / groups, hg = member % groups;
   const int s = a.shard_begin + s_local;
-  const int T = a.seq_lens[b];
-  const int t_begin = c * a.chunk_tokens;
-  if (t_begin >= T) return;
-  const int t_end = min(T, t_begin + a.chunk_tokens);
+
+  // Work of this workgroup.  Chunked schedule: unit u is chunk c of sequence b (one segment).
+  // Balanced schedule: unit u is worker u, which takes the u-th equal share of all 32-token
+  // tiles of the batch (tile_prefix[b] = tiles of sequences before b; min(workers, tiles)
+  // workers take part) and works through it sequence by sequence; its partial for sequence b
+  // goes to slot b + u.
+  int64_t g_next = 0, g_end = 0;
+  if (a.sched == 1) {
+    // min(workers, tiles) workers take part, so that every share holds at least one tile
+    const int64_t total = a.tile_prefix[a.batch];
+    const int64_t nw = min(static_cast<int64_t>(units), total);
+    if (u >= nw) return;
+    g_next = static_cast<int64_t>(u) * total / nw;
+    g_end = static_cast<int64_t>(u + 1) * total / nw;
+  }
+  for (;;) {
+  int b, t_begin, t_end;
+  int64_t part_row0;  // partial row of head 0 of this segment
+  if (a.sched == 0) {
+    const int c = u % a.num_chunks;
+    b = u / a.num_chunks;
+    t_begin = c * a.chunk_tokens;
+    const int T = a.seq_lens[b];
+    if (t_begin >= T) return;
+    t_end = min(T, t_begin + a.chunk_tokens);
+    part_row0 = ((static_cast<int64_t>(b) * a.num_chunks + c) * a.shard_count + s_local) * a.heads;
+  } else {
+    if (g_next >= g_end) return;
+    // sequence holding global tile g_next: the last b with tile_prefix[b] <= g_next
+    int lo = 0, hi = a.batch;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.tile_prefix[mid] <= g_next) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    const int64_t p0 = a.tile_prefix[b], p1 = a.tile_prefix[b + 1];
+    const int64_t seg_end = min(g_end, p1);
+    t_begin = static_cast<int>((g_next - p0) * kNT);
+    t_end = min(a.seq_lens[b], static_cast<int>((seg_end - p0) * kNT));
+    part_row0 = ((static_cast<int64_t>(b) + u) * a.shard_count + s_local) * a.heads;
+    g_next = seg_end;
+  }
   const int n_tiles = (t_end - t_begin + kNT - 1) / kNT;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -519,7 +556,7 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
   // Chunk result: o = O / l, lse = ln 2 * (m + log2 l); the two lane halves hold disjoint tokens.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
-  const int64_t part = ((static_cast<int64_t>(b) * a.num_chunks + c) * a.shard_count + s_local) * a.heads + head;
+  const int64_t part = part_row0 + head;
   float* dst = a.part_o + part * W;
 #pragma unroll
   for (int cbl = 0; cbl < C::CB; ++cbl) {
@@ -533,6 +570,9 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
     }
   }
   if (half == 0 && kh == 0) a.part_lse[part] = (m_ref + log2f(l_tot)) * kLn2;
+  if (a.sched == 0) return;  // a chunk is a single segment
+  __syncthreads();           // the next segment reuses the ring and the page list
+  }
 }
 
 template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
@@ -542,7 +582,7 @@ hipError_t launch_one(const DecodeLaunch& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  const int units = a.num_chunks * a.batch;
+  const int units = a.sched == 1 ? a.workers : a.num_chunks * a.batch;
   const int members = a.shard_count * (a.heads / (32 * HB));
   const int64_t blocks = static_cast<int64_t>((units + 7) / 8) * 8 * members;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -614,10 +654,12 @@ void mfma_plan_info(int w, int heads, int* head_groups, int* wgs_per_cu) {
 
 int mfma_max_chunk_pages() { return kMaxPages - 2; }
 
+int mfma_max_segment_pages() { return kMaxPages - 2; }
+
 hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t stream) {
   if (!mfma_supported(a.w, a.d_rope, a.heads)) return hipErrorInvalidValue;
   // the chunk's block-table entries must fit the LDS page list
-  if (a.block_table != nullptr && a.chunk_tokens / a.page_size + 2 > kMaxPages) return hipErrorInvalidValue;
+  if (a.block_table != nullptr && a.sched == 0 && a.chunk_tokens / a.page_size + 2 > kMaxPages) return hipErrorInvalidValue;
   switch (a.w) {
     case 128: return launch_w<128, kW128.hb_max, kW128.ks, kW128.st>(a, stream);
     case 256: return launch_w<256, kW256.hb_max, kW256.ks, kW256.st>(a, stream);

@@ -25,6 +25,15 @@ struct DecodeLaunch {
   int chunk_tokens, num_chunks;
   float* part_o;
   float* part_lse;
+  // Balanced schedule (sched = 1, MFMA kernel): min(workers, tiles) workgroups per (shard, head
+  // group) take equal shares of all 32-token tiles of the batch; tile_prefix[b] (b = 0..batch)
+  // counts the tiles of the sequences before b.  The partial of sequence b from worker w is
+  // slot b + w:
+  //   part_o [((b + w) * shard_count + s_local) * heads + h] * w_cols   (w_cols = w floats)
+  // Chunked schedule (sched = 0): chunk c of sequence b is slot b * num_chunks + c.
+  int sched;
+  int workers;
+  const int* tile_prefix;
 };
 
 struct MergeLaunch {
@@ -34,6 +43,8 @@ struct MergeLaunch {
   int batch, heads, d_latent, w;
   int shard_begin, shard_count;
   int chunk_tokens, num_chunks;
+  int sched, workers;
+  const int* tile_prefix;
   int wht;
   float* out;
   float* lse;   // may be null
@@ -49,6 +60,10 @@ void mfma_plan_info(int w, int heads, int* head_groups, int* wgs_per_cu);
 // Largest number of cache pages one chunk of the MFMA kernel may span.
 int mfma_max_chunk_pages();
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
+// tile_prefix[b] = sum over b' < b of ceil(seq_lens[b'] / 32), b = 0..batch.
+hipError_t launch_tile_prefix(const int* seq_lens, int batch, int* tile_prefix, hipStream_t stream);
+// Largest number of cache pages one segment of the MFMA kernel may span (its LDS page list).
+int mfma_max_segment_pages();
 // Rotate q_lat [B*H, d_c] by the Hadamard matrix into dst (fp32 if dst_f32, else bf16).
 hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_latent, void* dst, int dst_f32,
                                hipStream_t stream);

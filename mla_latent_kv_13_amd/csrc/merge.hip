@@ -76,8 +76,23 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
   const int h = blockIdx.x * kMergeWaves + wv, b = blockIdx.y;
   if (h >= a.heads) return;  // the rest of this kernel is wave-local
   float* y = ybuf[wv];
-  const int T = a.seq_lens[b];
-  const int nv = (T + a.chunk_tokens - 1) / a.chunk_tokens;  // chunks holding tokens
+  // Partials of sequence b: nv consecutive slots from slot0 (chunks holding tokens, or the
+  // workers whose tile share meets the sequence under the balanced schedule).
+  int nv;
+  int64_t slot0;
+  if (a.sched == 0) {
+    const int T = a.seq_lens[b];
+    nv = (T + a.chunk_tokens - 1) / a.chunk_tokens;
+    slot0 = static_cast<int64_t>(b) * a.num_chunks;
+  } else {
+    const int64_t total = a.tile_prefix[a.batch];
+    const int64_t p0 = a.tile_prefix[b], p1 = a.tile_prefix[b + 1];
+    const int64_t nw = min(static_cast<int64_t>(a.workers), total);  // workers that took part
+    // worker holding tile t: the largest w with floor(w * total / nw) <= t
+    auto worker_of = [&](int64_t t) { return ((t + 1) * nw - 1) / total; };
+    nv = p1 > p0 ? static_cast<int>(worker_of(p1 - 1) - worker_of(p0) + 1) : 0;
+    slot0 = p1 > p0 ? b + worker_of(p0) : 0;
+  }
   const int lo = a.shard_begin * a.w, hi = lo + a.shard_count * a.w;
   for (int j = lane; j < a.d_latent; j += 64)
     if (j < lo || j >= hi) y[j] = 0.f;  // latent columns of shards that were not computed
@@ -86,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
   const int wv_cols = a.w / V;                                              // vectors per slice row
   for (int sl = 0; sl < a.shard_count; ++sl) {
     const int s = a.shard_begin + sl;
-    const int64_t base = (static_cast<int64_t>(b) * a.num_chunks * a.shard_count + sl) * a.heads + h;
+    const int64_t base = (slot0 * a.shard_count + sl) * a.heads + h;
     float mx = -INFINITY;
     for (int k = lane; k < nv; k += 64) mx = fmaxf(mx, a.part_lse[base + k * stride]);
     const float M = wave_max(mx);
@@ -162,7 +177,37 @@ __global__ __launch_bounds__(kThreads) void rotate_query_kernel(const T* __restr
   }
 }
 
+// tile_prefix[b] = sum_{b' < b} ceil(seq_lens[b'] / 32) for b = 0..batch, one block: each thread
+// sums a contiguous run of sequences, then an exclusive scan over the threads' sums.
+__global__ __launch_bounds__(kThreads) void tile_prefix_kernel(const int* __restrict__ seq_lens, int batch,
+                                                               int* __restrict__ prefix) {
+  __shared__ int sums[kThreads];
+  const int per = (batch + kThreads - 1) / kThreads;
+  const int b0 = threadIdx.x * per, b1 = min(batch, b0 + per);
+  int own = 0;
+  for (int b = b0; b < b1; ++b) own += (seq_lens[b] + 31) >> 5;
+  sums[threadIdx.x] = own;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan (Hillis-Steele)
+    const int v = threadIdx.x >= off ? sums[threadIdx.x - off] : 0;
+    __syncthreads();
+    sums[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = sums[threadIdx.x] - own;  // exclusive
+  for (int b = b0; b < b1; ++b) {
+    prefix[b] = run;
+    run += (seq_lens[b] + 31) >> 5;
+  }
+  if (threadIdx.x == kThreads - 1) prefix[batch] = sums[kThreads - 1];
+}
+
 }  // namespace
+
+hipError_t launch_tile_prefix(const int* seq_lens, int batch, int* tile_prefix, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(kThreads), 0, stream, seq_lens, batch, tile_prefix);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
   if (a.d_latent > kMaxLatent) return hipErrorInvalidValue;

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert binding.abi_version() == 1
+    assert binding.abi_version() == 2
     assert lib.tpla_status_string(3) == b"TPLA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -49,7 +49,11 @@ def test_workspace_size_host_only(lib):
     assert n > 16 * 2 * 128 * 256 * 4  # at least one chunk of partials per sequence and shard
     rot = binding.Desc("bf16", 512, 64, 64, 1000, 1024, "wht")
     assert binding.workspace_size(rot, 16, 128, 2, 2, 32768) > n  # room for the rotated query
-    assert binding.workspace_size(DSV3, 16, 128, 2, 2, 32768, chunk_tokens=64) > n
+    # a paged cache uses the balanced schedule by default, which ignores chunk_tokens
+    assert binding.workspace_size(DSV3, 16, 128, 2, 2, 32768, chunk_tokens=64) == n
+    chunked = binding.workspace_size(DSV3, 16, 128, 2, 2, 32768, schedule="chunked")
+    assert binding.workspace_size(DSV3, 16, 128, 2, 2, 32768, chunk_tokens=64, schedule="chunked") > chunked
+    assert binding.workspace_size(DSV3, 16, 128, 2, 2, 32768, schedule="balanced") == n
 
 
 @pytest.mark.parametrize("kw,msg", [
@@ -58,15 +62,17 @@ def test_workspace_size_host_only(lib):
     (dict(heads=0), "INVALID_ARGUMENT"),
     (dict(chunk_tokens=100), "INVALID_ARGUMENT"),
     (dict(kernel="mfma", heads=40), "UNSUPPORTED"),
+    (dict(kernel="generic", schedule="balanced"), "UNSUPPORTED"),  # balanced needs the MFMA kernel
 ])
 def test_workspace_size_rejects(lib, kw, msg):
-    args = dict(batch=2, heads=128, num_shards=2, shard_count=None, max_seq_len=4096, chunk_tokens=0, kernel="auto")
+    args = dict(batch=2, heads=128, num_shards=2, shard_count=None, max_seq_len=4096, chunk_tokens=0, kernel="auto",
+                schedule="auto")
     args.update(kw)
     if args["shard_count"] is None:
         args["shard_count"] = args["num_shards"]
     with pytest.raises(binding.TplaError, match=msg):
         binding.workspace_size(DSV3, args["batch"], args["heads"], args["num_shards"], args["shard_count"],
-                               args["max_seq_len"], args["chunk_tokens"], args["kernel"])
+                               args["max_seq_len"], args["chunk_tokens"], args["kernel"], args["schedule"])
 
 
 def _decode_raw(lib, desc, **kw):

@@ -118,6 +118,38 @@ def test_bitwise_deterministic():
         assert torch.equal(first, again) and torch.equal(first_lse, again_lse)
 
 
+BALANCED = [
+    ("contig_ragged_g2", dict(batch=5, heads=128, shards=2, lens=[1000, 0, 1, 4097, 33])),
+    ("paged_ragged_g1", dict(batch=4, heads=128, shards=1, lens=[2500, 31, 0, 700], paged=True, page_size=64,
+                             extra_pages=3)),
+    ("paged16_ragged_g4_wht", dict(batch=3, heads=64, shards=4, lens=[900, 64, 3], paged=True, page_size=16,
+                                   transform="wht")),
+    ("more_workers_than_tiles", dict(batch=6, heads=32, shards=1, lens=[5, 0, 40, 1, 0, 70])),
+    ("all_empty", dict(batch=3, heads=64, shards=2, lens=[0, 0, 0])),
+]
+
+
+@pytest.mark.parametrize("name,kw", BALANCED, ids=[b[0] for b in BALANCED])
+def test_balanced_and_chunked_schedules_match_oracle(name, kw):
+    """Both work schedules of the MFMA kernel on ragged batches (empty, single-token, multi-page
+    sequences; shares of tiles crossing sequence boundaries) against the oracle."""
+    _say(f"case {name}")
+    args = dict(d_latent=512, d_rope=64, dtype="bf16", scale=1.0 / np.sqrt(192))
+    args.update(kw)
+    case = inputs.make_case(300 + len(name), name=name, **args)
+    dc = DeviceCase(case)
+    ref_out, ref_lse = oracle_decode(case)
+    outs = {}
+    for sched in ("chunked", "balanced"):
+        out, lse = dc.decode(schedule=sched, chunk_tokens=128 if sched == "chunked" else 0)
+        torch.cuda.synchronize()
+        assert_parity(_np(out), ref_out, "bf16", f"{name} {sched}")
+        assert_lse(_np(lse), ref_lse, "bf16", f"{name} {sched}", case.transform)
+        outs[sched] = _np(out)
+    rel, _ = parity(outs["balanced"], outs["chunked"])
+    assert rel < 5e-3
+
+
 def test_split_count_invariance():
     case = inputs.make_case(11, batch=2, heads=128, d_latent=512, d_rope=64, shards=2, lens=[4096, 1500])
     dc = DeviceCase(case)
