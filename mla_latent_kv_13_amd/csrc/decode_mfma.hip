@@ -50,7 +50,7 @@ constexpr int kMaxPages = 1024;  // block-table entries of one chunk kept in LDS
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-template <int W, int DR, int HB, int KS, int STQ>
+template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
 struct Cfg {
   static constexpr int KW = W + DR;                // key width of one shard
   static constexpr int ROW_BYTES = KW * 2;
@@ -63,14 +63,21 @@ struct Cfg {
   static constexpr int PER_LO = INSTR / NWAVES;    // pieces per wave; the first REM waves take one more
   static constexpr int REM = INSTR % NWAVES;
   static constexpr int PER_MAX = PER_LO + (REM ? 1 : 0);
-  // ring stages: as requested, but never more loads in flight per lane than vmcnt can count (63)
-  static constexpr int ST = STQ < 2 + 63 / PER_MAX ? STQ : 2 + 63 / PER_MAX;
   static constexpr int KSTEPS = KW / 16 / KS;      // QK k-steps of one wave
   static constexpr int CB = W / 32 / KS;           // 32-column value blocks of one wave
-  static constexpr int SX_OFF = ST * TILE_BYTES;   // partial-logit exchange (KS > 1)
-  static constexpr int SX_BYTES = KS > 1 ? 2 * NWAVES * 4096 : 0;  // double-buffered by tile parity
+  // LDS: ST ring stages, SXB buffers of the partial-logit exchange (KS > 1; two = by tile parity),
+  // the page list of paged layouts.  Ring stages: as requested, but never more loads in flight
+  // per lane than vmcnt can count (63), and only as many as fit with at least one exchange buffer.
+  static constexpr int PAGE_BYTES = LAYOUT != 0 ? kMaxPages * 4 : 0;
+  static constexpr int SX_ONE = KS > 1 ? NWAVES * 4096 : 0;
+  static constexpr bool fits(int st, int sxb) { return st * TILE_BYTES + sxb * SX_ONE + PAGE_BYTES <= 160 * 1024; }
+  static constexpr int ST0 = STQ < 2 + 63 / PER_MAX ? STQ : 2 + 63 / PER_MAX;
+  static constexpr int ST = fits(ST0, 1) ? ST0 : (fits(ST0 - 1, 1) ? ST0 - 1 : ST0 - 2);
+  static constexpr int SXB = KS > 1 && !fits(ST, 2) ? 1 : 2;
+  static constexpr int SX_OFF = ST * TILE_BYTES;
+  static constexpr int SX_BYTES = SXB * SX_ONE;
   static constexpr int PAGES_OFF = SX_OFF + SX_BYTES;
-  static constexpr int LDS_BYTES = PAGES_OFF + kMaxPages * 4;
+  static constexpr int LDS_BYTES = PAGES_OFF + PAGE_BYTES;
   static_assert(W % 32 == 0 && DR % 16 == 0 && CPR % 8 == 0, "tile shape");
   static_assert(kNT * CPR % 64 == 0, "a tile is a whole number of 1 KiB pieces");
   static_assert((KW / 16) % KS == 0 && (W / 32) % KS == 0, "key/value split");
@@ -125,7 +132,7 @@ __device__ __forceinline__ void raw_barrier() {
 template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
 __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaunch a, float scale_log2, int units,
                                                                        int members, int page_shift) {
-  using C = Cfg<W, DR, HB, KS, STQ>;
+  using C = Cfg<W, DR, HB, KS, STQ, LAYOUT>;
   constexpr int ST = C::ST;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
 
@@ -338,14 +345,14 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a_op), __builtin_bit_cast(bf16x8_t, b_op),
                                                    c_acc, 0, 0, 0);
   };
-  // Partial logits of a wave pair (KS = 2), double-buffered by tile parity.
+  // Partial logits of a wave pair (KS = 2), double-buffered by tile parity when LDS allows.
   auto sx_write = [&](int par, const floatx16_t& v) {
-    float4* dst = reinterpret_cast<float4*>(lds + C::SX_OFF + (par * C::NWAVES + wv) * 4096);
+    float4* dst = reinterpret_cast<float4*>(lds + C::SX_OFF + ((par % C::SXB) * C::NWAVES + wv) * 4096);
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) dst[j4 * 64 + lane] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
   };
   auto sx_read = [&](int par, float4 (&pv)[4]) {
-    const float4* src = reinterpret_cast<const float4*>(lds + C::SX_OFF + (par * C::NWAVES + (wv ^ 1)) * 4096);
+    const float4* src = reinterpret_cast<const float4*>(lds + C::SX_OFF + ((par % C::SXB) * C::NWAVES + (wv ^ 1)) * 4096);
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) pv[j4] = src[j4 * 64 + lane];
   };
@@ -470,6 +477,8 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
 
       float x[16];
       logits(s_cur, pvx, x);
+      // one exchange buffer: every wave has its partner's partial logits before any overwrites them
+      if constexpr (KS > 1 && C::SXB == 1) raw_barrier();
       const float m_old = m_ref;
       float neg_m;
       alpha = softmax_max(x, neg_m);
@@ -577,7 +586,7 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
 
 template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
 hipError_t launch_one(const DecodeLaunch& a, hipStream_t stream) {
-  using C = Cfg<W, DR, HB, KS, STQ>;
+  using C = Cfg<W, DR, HB, KS, STQ, LAYOUT>;
   auto kern = decode_mfma_kernel<W, DR, HB, KS, STQ, LAYOUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      C::LDS_BYTES);
@@ -610,7 +619,7 @@ hipError_t launch_layout(const DecodeLaunch& a, hipStream_t stream) {
 #define TPLA_W256_CFG 4, 1, 6
 #endif
 #ifndef TPLA_W512_CFG
-#define TPLA_W512_CFG 2, 2, 3
+#define TPLA_W512_CFG 2, 2, 4
 #endif
 struct TileCfg {
   int hb_max, ks, st;
