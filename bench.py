@@ -140,13 +140,25 @@ class Workload:
         return d
 
 
+_FLUSH = []
+
+
+def _flush_buffer():
+    """A 1 GiB device buffer whose full read evicts the 256 MB last-level cache; allocated once."""
+    import torch
+
+    if not _FLUSH:
+        _FLUSH.append(torch.zeros(1 << 28, dtype=torch.float32, device="cuda:0"))
+    return _FLUSH[0]
+
+
 def time_workload(w: Workload, steps: int, warmup: int, flush: bool):
     """Time `steps` whole calls (events around the call only), then the split-K decode kernel
     alone in `steps` further calls (events the library records around that kernel).  Event
     markers inside a call cost it several microseconds, so the two are measured apart."""
     import torch
 
-    flush_buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda:0") if flush else None
+    flush_buf = _flush_buffer() if flush else None
 
     def evict():
         if flush_buf is not None:
@@ -288,7 +300,7 @@ def main():
             if cfg == args.config:
                 continue
             w = Workload(cfg, args.chunk_tokens)
-            r = time_workload(w, args.extra_steps, 2, not args.no_flush)
+            r = time_workload(w, args.extra_steps, args.warmup, not args.no_flush)
             others[w.case.name] = {"config": w.config(), "tokens_per_s": r["tokens_per_s"],
                                    "call_ms_mean": r["call_ms_mean"], "hbm_gbs": r["call_gbs"],
                                    "hbm_frac_of_peak": r["call_gbs"] / HBM_PEAK_GBS,

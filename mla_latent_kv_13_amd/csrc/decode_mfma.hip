@@ -65,17 +65,15 @@ struct Cfg {
   static constexpr int PER_MAX = PER_LO + (REM ? 1 : 0);
   static constexpr int KSTEPS = KW / 16 / KS;      // QK k-steps of one wave
   static constexpr int CB = W / 32 / KS;           // 32-column value blocks of one wave
-  // LDS: ST ring stages, SXB buffers of the partial-logit exchange (KS > 1; two = by tile parity),
-  // the page list of paged layouts.  Ring stages: as requested, but never more loads in flight
-  // per lane than vmcnt can count (63), and only as many as fit with at least one exchange buffer.
+  // LDS: ST ring stages, the partial-logit exchange buffer (KS > 1), the page list of paged
+  // layouts.  Ring stages: as requested, but never more loads in flight per lane than vmcnt can
+  // count (63), and only as many as fit.
   static constexpr int PAGE_BYTES = LAYOUT != 0 ? kMaxPages * 4 : 0;
-  static constexpr int SX_ONE = KS > 1 ? NWAVES * 4096 : 0;
-  static constexpr bool fits(int st, int sxb) { return st * TILE_BYTES + sxb * SX_ONE + PAGE_BYTES <= 160 * 1024; }
+  static constexpr int SX_BYTES = KS > 1 ? NWAVES * 4096 : 0;
+  static constexpr bool fits(int st) { return st * TILE_BYTES + SX_BYTES + PAGE_BYTES <= 160 * 1024; }
   static constexpr int ST0 = STQ < 2 + 63 / PER_MAX ? STQ : 2 + 63 / PER_MAX;
-  static constexpr int ST = fits(ST0, 1) ? ST0 : (fits(ST0 - 1, 1) ? ST0 - 1 : ST0 - 2);
-  static constexpr int SXB = KS > 1 && !fits(ST, 2) ? 1 : 2;
+  static constexpr int ST = fits(ST0) ? ST0 : (fits(ST0 - 1) ? ST0 - 1 : ST0 - 2);
   static constexpr int SX_OFF = ST * TILE_BYTES;
-  static constexpr int SX_BYTES = SXB * SX_ONE;
   static constexpr int PAGES_OFF = SX_OFF + SX_BYTES;
   static constexpr int LDS_BYTES = PAGES_OFF + PAGE_BYTES;
   static_assert(W % 32 == 0 && DR % 16 == 0 && CPR % 8 == 0, "tile shape");
@@ -345,14 +343,15 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a_op), __builtin_bit_cast(bf16x8_t, b_op),
                                                    c_acc, 0, 0, 0);
   };
-  // Partial logits of a wave pair (KS = 2), double-buffered by tile parity when LDS allows.
-  auto sx_write = [&](int par, const floatx16_t& v) {
-    float4* dst = reinterpret_cast<float4*>(lds + C::SX_OFF + ((par % C::SXB) * C::NWAVES + wv) * 4096);
+  // Partial logits of a wave pair (KS = 2): one buffer, written after a tile's logit product and
+  // read by the partner after the barrier that follows the write.
+  auto sx_write = [&](const floatx16_t& v) {
+    float4* dst = reinterpret_cast<float4*>(lds + C::SX_OFF + wv * 4096);
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) dst[j4 * 64 + lane] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
   };
-  auto sx_read = [&](int par, float4 (&pv)[4]) {
-    const float4* src = reinterpret_cast<const float4*>(lds + C::SX_OFF + ((par % C::SXB) * C::NWAVES + (wv ^ 1)) * 4096);
+  auto sx_read = [&](float4 (&pv)[4]) {
+    const float4* src = reinterpret_cast<const float4*>(lds + C::SX_OFF + (wv ^ 1) * 4096);
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) pv[j4] = src[j4 * 64 + lane];
   };
@@ -371,10 +370,12 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
   };
   // First half of the online softmax of a tile: the new reference maximum (over both lane halves,
   // i.e. all 32 tokens of the lane's head) and the rescale factor alpha of O and l (exactly 1
-  // unless the reference was raised).  Masked logits must be -inf here.
-  auto softmax_max = [&](const float (&x)[16], float& neg_m) {
-    float rmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    rmax = fmaxf(rmax, fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])), fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
+  // unless the reference was raised).  Tokens past the end of a partial tile may take part: their
+  // rows repeat the last valid row, so they do not change the maximum.
+  auto max8 = [](const float (&x)[16], int o) {
+    return fmaxf(fmaxf(fmaxf(x[o], x[o + 1]), fmaxf(x[o + 2], x[o + 3])), fmaxf(fmaxf(x[o + 4], x[o + 5]), fmaxf(x[o + 6], x[o + 7])));
+  };
+  auto max_final = [&](float rmax, float& neg_m) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
     rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     const float tmax = rmax * cs;
@@ -384,6 +385,7 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
     neg_m = -m_new;
     return alpha;
   };
+  auto softmax_max = [&](const float (&x)[16], float& neg_m) { return max_final(fmaxf(max8(x, 0), max8(x, 8)), neg_m); };
   // Second half, one pair of logits: p = 2^(cs*x - m_ref), packed to bf16 for the value product.
   auto softmax_pair = [&](const float (&x)[16], int j, float neg_m, uint32_t (&pk)[8], float& ps) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m));
@@ -409,6 +411,38 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // The value product of one tile with the softmax maximum of the next tile riding on its steps:
+  // (KS = 2) the barrier that publishes the pair's partial logits and the read of the partner's,
+  // then the logit sum, the maximum and the new reference.  sn = this wave's logits of the next
+  // tile; writes its full logits to x and its -m to neg_m, returns its alpha.
+  auto pv_next = [&](const unsigned char* tile, const uint32_t (&pk)[8], short8_t (&vf)[NPV], const floatx16_t& sn,
+                     float (&x)[16], float& neg_m) {
+    constexpr int VB = 1;                  // exchange barrier and partner read
+    constexpr int VL = NV >= 12 ? 5 : 3;   // logit sum, the partner's logits having arrived
+    constexpr int VF = VL + 3;             // last reduction step, new reference and alpha
+    static_assert(VF < NV, "value steps to carry the maximum");
+    const uint4 pb[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
+    float4 pvx[4];
+    float rmax = 0.f, alpha = 1.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if constexpr (KS > 1) {
+        if (v == VB) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own partial logits written
+          raw_barrier();
+          sx_read(pvx);
+        }
+      }
+      o_acc[v % C::CB] = mfma(vf[v % NPV], pb[v / C::CB], o_acc[v % C::CB]);
+      if (v + NPV < NV) vf[v % NPV] = vread(tile, v + NPV);
+      if (v == VL) logits(sn, pvx, x);
+      if (v == VL + 1) rmax = max8(x, 0);
+      if (v == VL + 2) rmax = fmaxf(rmax, max8(x, 8));
+      if (v == VF) alpha = max_final(rmax, neg_m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return alpha;
+  };
 
   // Tile j sits in ring stage j % ST.  Waiting for tile j when `newer` tiles were issued after
   // it: the loads of those may stay in flight, which the wait can express only for the steady
@@ -425,45 +459,54 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
     }
   };
 
-  // Prologue: tiles 0..ST-2 are in flight.  Wait for tile 0 and compute its logits.
+  // Prologue: tiles 0..ST-2 are in flight.  Wait for tile 0, compute its logits and maximum.
   wait_tile(min(n_tiles - 1, ST - 2), std::integral_constant<int, ST - 2>{});
   raw_barrier();
-  floatx16_t s_cur;
+  // Softmax state of the tile about to be weighted: its full logits x (unscaled), -m_ref and
+  // alpha, the factor O and l take before its weights are added.
+  float x[16], neg_m, alpha;
   {
     const unsigned char* t0 = tile_at(0);
     uint4 kf[NPF];
 #pragma unroll
     for (int k = 0; k < NPF; ++k) kf[k] = kread(t0, k);
+    floatx16_t s0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s_cur[j] = 0.f;
+    for (int j = 0; j < 16; ++j) s0[j] = 0.f;
 #pragma unroll
     for (int k = 0; k < KST; ++k) {
-      s_cur = mfma(kf[k % NPF], qf[k], s_cur);
+      s0 = mfma(kf[k % NPF], qf[k], s0);
       if (k + NPF < KST) kf[k % NPF] = kread(t0, k + NPF);
     }
-    if constexpr (KS > 1) sx_write(0, s_cur);
+    float4 pvx[4];
+    if constexpr (KS > 1) {
+      sx_write(s0);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      raw_barrier();
+      sx_read(pvx);
+    }
+    logits(s0, pvx, x);
+    alpha = softmax_max(x, neg_m);  // the first tile: O and l are still zero
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // Steady state, tile i with tile i+1 resident.  Each k-step of the logits of tile i+1 (one
-  // MFMA) also carries one read-ahead K fragment, up to one pair of tile i's softmax and, in the
-  // last NPV steps, one value fragment of tile i; then comes tile i's value product, each MFMA
-  // with one read-ahead value fragment.  The steps are fenced so that the compiler keeps this
-  // order, which hides the LDS latency behind the matrix cores and the softmax arithmetic in the
-  // gaps between MFMA issues.
-  // A tile that raises the reference maximum (other than the first: O is still zero then) leaves
-  // the inner loop before its value product, so that the rescale of O -- which needs O out of the
-  // accumulation registers -- stays outside the steady-state loop.
+  // Steady state, iteration i: tile i with tile i+1 resident.  Each k-step of the logits of tile
+  // i+1 (one MFMA) also carries one read-ahead K fragment, up to one pair of tile i's softmax
+  // weights and, in the last NPV steps, one value fragment of tile i; then comes tile i's value
+  // product, whose steps carry the maximum of tile i+1 (with the pair's exchange at KS = 2).  The
+  // steps are fenced so that the compiler keeps this order, which hides the LDS latency behind
+  // the matrix cores and the softmax arithmetic in the gaps between MFMA issues.
+  // When tile i+1 raises the reference maximum (rare), the iteration leaves the inner loop after
+  // its value product, so that the rescale of O -- which needs O out of the accumulation
+  // registers -- stays outside the steady-state loop.
   int st_cur = 0, st_next = 1 % ST, st_issue = ST - 1;
   int i = 0;
-  floatx16_t s_nxt;
   uint32_t pk[8];
-  float alpha = 1.0f;
   while (i + 1 < n_tiles) {
     bool raised = false;
     for (; i + 1 < n_tiles; ++i) {
       wait_tile(min(n_tiles - 1, ST + i - 2) - (i + 1), std::integral_constant<int, ST - 3>{});
-      raw_barrier();  // tile i+1 visible; tile i-1's stage free; partial logits of tile i visible
+      raw_barrier();  // tile i+1 visible; tile i-1's stage and the exchange buffer free
       if (i + ST - 1 < n_tiles) issue(i + ST - 1, st_issue);
       st_issue = st_issue + 1 == ST ? 0 : st_issue + 1;
       const unsigned char* tn = tile_at(st_next);
@@ -471,19 +514,9 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
       uint4 kf[NPF];
 #pragma unroll
       for (int k = 0; k < NPF; ++k) kf[k] = kread(tn, k);
-      float4 pvx[4];
-      if constexpr (KS > 1) sx_read(i & 1, pvx);
       __builtin_amdgcn_sched_barrier(0);
 
-      float x[16];
-      logits(s_cur, pvx, x);
-      // one exchange buffer: every wave has its partner's partial logits before any overwrites them
-      if constexpr (KS > 1 && C::SXB == 1) raw_barrier();
-      const float m_old = m_ref;
-      float neg_m;
-      alpha = softmax_max(x, neg_m);
-      __builtin_amdgcn_sched_barrier(0);
-
+      floatx16_t s_nxt;
 #pragma unroll
       for (int j = 0; j < 16; ++j) s_nxt[j] = 0.f;
       float ps = 0.f;
@@ -499,62 +532,38 @@ __global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaun
         __builtin_amdgcn_sched_barrier(0);
       }
       l_run = __builtin_fmaf(l_run, alpha, ps);
-      if constexpr (KS > 1) sx_write((i + 1) & 1, s_nxt);
-      if (__any(alpha != 1.0f && m_old != -INFINITY)) {  // wave-uniform, rare
-        raised = true;
-        break;
-      }
+      if constexpr (KS > 1) sx_write(s_nxt);
+      const float m_old = m_ref;
       __builtin_amdgcn_sched_barrier(0);
-      pv(tc, pk, vf);
-      s_cur = s_nxt;
+      alpha = pv_next(tc, pk, vf, s_nxt, x, neg_m);
       st_cur = st_next;
       st_next = st_next + 1 == ST ? 0 : st_next + 1;
+      if (__any(alpha != 1.0f && m_old != -INFINITY)) {  // wave-uniform, rare
+        raised = true;
+        ++i;
+        break;
+      }
     }
     if (!raised) break;
-    // finish tile i after raising the reference maximum
-    rescale(alpha);
-    const unsigned char* tc = tile_at(st_cur);
-    short8_t vf[NPV];
-#pragma unroll
-    for (int v = 0; v < NPV; ++v) vf[v] = vread(tc, v);
-    pv(tc, pk, vf);
-    s_cur = s_nxt;
-    st_cur = st_next;
-    st_next = st_next + 1 == ST ? 0 : st_next + 1;
-    ++i;
+    rescale(alpha);  // before tile i's weights are added
   }
 
-  // Last tile (possibly partial): mask tokens past the end, then its softmax and value product.
+  // Last tile (possibly partial): weights of the tokens past the end are exactly 0, also when
+  // the scale is zero.  Its maximum is known and O already rescaled.
   {
     const int i = n_tiles - 1;
-    float4 pvx[4];
-    if constexpr (KS > 1) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own partial logits written
-      raw_barrier();
-      sx_read(i & 1, pvx);
-    }
     const int valid = t_end - (t_begin + i * kNT);
-    float x[16];
-    logits(s_cur, pvx, x);
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (8 * (j >> 2) + 4 * half + (j & 3) >= valid) x[j] = -INFINITY;  // token 0 is always valid
-    float neg_m;
-    const float alpha = softmax_max(x, neg_m);
-    uint32_t pk[8];
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bool k0 = 8 * ((2 * j) >> 2) + 4 * half + ((2 * j) & 3) < valid;
       const bool k1 = 8 * ((2 * j + 1) >> 2) + 4 * half + ((2 * j + 1) & 3) < valid;
-      // masked tokens weigh exactly 0, also when the scale is zero
       const float p0 = k0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m)) : 0.f;
       const float p1 = k1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m)) : 0.f;
       ps += p0 + p1;
       pk[j] = pack_bf16x2(p0, p1);
     }
     l_run = __builtin_fmaf(l_run, alpha, ps);
-    if (__any(alpha != 1.0f)) rescale(alpha);
     const unsigned char* tile = tile_at(st_cur);
     short8_t vf[NPV];
 #pragma unroll
