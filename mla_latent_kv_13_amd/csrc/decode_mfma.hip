@@ -50,6 +50,11 @@ constexpr int kMaxPages = 1024;  // block-table entries of one chunk kept in LDS
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
+// Waves per SIMD a configuration is built for: two where a wave's registers fit half the file
+// (value width 128 with at least two head blocks of 32), else one.  Two waves per SIMD let one
+// wave's barrier, LDS and softmax stalls be covered by the other's matrix work.
+constexpr int waves_per_simd(int w, int hb, int ks) { return w == 128 && hb >= 2 && ks == 1 ? 2 : 1; }
+
 template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
 struct Cfg {
   static constexpr int KW = W + DR;                // key width of one shard
@@ -65,14 +70,18 @@ struct Cfg {
   static constexpr int PER_MAX = PER_LO + (REM ? 1 : 0);
   static constexpr int KSTEPS = KW / 16 / KS;      // QK k-steps of one wave
   static constexpr int CB = W / 32 / KS;           // 32-column value blocks of one wave
-  // LDS: ST ring stages, the partial-logit exchange buffer (KS > 1), the page list of paged
-  // layouts.  Ring stages: as requested, but never more loads in flight per lane than vmcnt can
-  // count (63), and only as many as fit.
+  // LDS a workgroup may take: all of it, or with two waves per SIMD its share among the
+  // workgroups that the CU then holds together.  It holds ST ring stages, the partial-logit
+  // exchange buffer (KS > 1), the page list of paged layouts.  Ring stages: as requested, but
+  // never more loads in flight per lane than vmcnt can count (63), and only as many as fit.
+  static constexpr int OCC = waves_per_simd(W, HB, KS);
+  static constexpr int LDS_BUDGET = OCC > 1 ? 160 * 1024 / ((NWAVES >= 4 ? 1 : 4 / NWAVES) * OCC) : 160 * 1024;
   static constexpr int PAGE_BYTES = LAYOUT != 0 ? kMaxPages * 4 : 0;
   static constexpr int SX_BYTES = KS > 1 ? NWAVES * 4096 : 0;
-  static constexpr bool fits(int st) { return st * TILE_BYTES + SX_BYTES + PAGE_BYTES <= 160 * 1024; }
+  static constexpr bool fits(int st) { return st * TILE_BYTES + SX_BYTES + PAGE_BYTES <= LDS_BUDGET; }
   static constexpr int ST0 = STQ < 2 + 63 / PER_MAX ? STQ : 2 + 63 / PER_MAX;
-  static constexpr int ST = fits(ST0) ? ST0 : (fits(ST0 - 1) ? ST0 - 1 : ST0 - 2);
+  static constexpr int largest_fit(int st) { return st <= 3 || fits(st) ? st : largest_fit(st - 1); }
+  static constexpr int ST = largest_fit(ST0);
   static constexpr int SX_OFF = ST * TILE_BYTES;
   static constexpr int PAGES_OFF = SX_OFF + SX_BYTES;
   static constexpr int LDS_BYTES = PAGES_OFF + PAGE_BYTES;
@@ -81,7 +90,7 @@ struct Cfg {
   static_assert((KW / 16) % KS == 0 && (W / 32) % KS == 0, "key/value split");
   static_assert(KS == 1 || KS == 2, "key split");
   static_assert(ST >= 3, "ring of at least three tiles (two resident, one in flight)");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES <= LDS_BUDGET, "LDS budget");
 };
 
 __device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
@@ -128,7 +137,7 @@ __device__ __forceinline__ void raw_barrier() {
 }
 
 template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
-__global__ __launch_bounds__(HB * KS * 64, 1) void decode_mfma_kernel(DecodeLaunch a, float scale_log2, int units,
+__global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decode_mfma_kernel(DecodeLaunch a, float scale_log2, int units,
                                                                        int members, int page_shift) {
   using C = Cfg<W, DR, HB, KS, STQ, LAYOUT>;
   constexpr int ST = C::ST;
@@ -664,10 +673,10 @@ bool mfma_supported(int w, int d_rope, int heads) {
 void mfma_plan_info(int w, int heads, int* head_groups, int* wgs_per_cu) {
   const int hb = pick_hb(w, heads);
   *head_groups = heads / (32 * hb);
-  // one wave per SIMD (the kernels use more than half the register file), so a CU holds
-  // 4 / (waves per workgroup) workgroups
+  // one wave per SIMD (or two, see waves_per_simd), so a CU holds 4 / (waves per workgroup)
+  // workgroups, times the waves per SIMD
   const int waves = hb * tile_cfg(w).ks;
-  *wgs_per_cu = waves >= 4 ? 1 : 4 / waves;
+  *wgs_per_cu = (waves >= 4 ? 1 : 4 / waves) * waves_per_simd(w, hb, tile_cfg(w).ks);
 }
 
 int mfma_max_chunk_pages() { return kMaxPages - 2; }
