@@ -37,7 +37,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "latent-cache decode tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "mla_latent_kv_13_amd", "csrc", "decode_mfma.hip")
+# the decode kernel's sources: its file and the LDS-DMA helpers it includes
+KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_13_amd", "csrc", f) for f in ("decode_mfma.hip", "lds_dma.h")]
 
 
 def log(msg):
@@ -200,18 +201,66 @@ def time_workload(w: Workload, steps: int, warmup: int, flush: bool):
     }
 
 
+def time_shard_calls(w: Workload, steps: int, warmup: int, flush: bool):
+    """The one-GPU view of TPLA's device split on a contiguous workload: the call of a single
+    shard (shard_begin = 0, shard_count = 1: the latent slice plus the rope, (w + d_r) * 2 bytes
+    per token, what one device of G would read) and the G = 1 call (exact MLA, all 576 values
+    per token) over the same cache, each timed like the full call (events around the call)."""
+    import torch
+
+    c = w.case
+    binding = w.binding
+    B, H = c.batch, c.heads
+    flush_buf = _flush_buffer() if flush else None
+    res = {}
+    for name, num_shards in (("one_shard_of_g", c.shards), ("g1_same_cache", 1)):
+        need = binding.workspace_size(w.desc, B, H, num_shards, 1, c.max_seq_len)
+        ws = binding.alloc_workspace(need, "cuda:0")
+        out = torch.empty((B, H, c.d_latent), dtype=torch.float32, device="cuda:0")
+        lse = torch.empty((B, 1, H), dtype=torch.float32, device="cuda:0")
+
+        def call():
+            binding.tpla_decode_sharded(w.desc, w.pool, w.block_table, w.seq_lens, w.q_lat, w.q_rope, c.scale,
+                                        num_shards, c.max_seq_len, shard_begin=0, shard_count=1, out=out, lse=lse,
+                                        workspace=ws)
+
+        for _ in range(warmup):
+            if flush_buf is not None:
+                flush_buf.sum()
+            call()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            if flush_buf is not None:
+                flush_buf.sum()
+            ev[i][0].record()
+            call()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
+        width = c.d_latent // num_shards + c.d_rope
+        nbytes = w.tokens * width * (2 if c.dtype == "bf16" else 4)
+        res[name] = {"shards": num_shards, "values_per_token": width, "call_ms_mean": ms,
+                     "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9}
+        del ws, out, lse
+    return res
+
+
 def traffic_for_current_kernel(workload_name: str):
     """HBM bytes per decode-kernel launch from the committed counter summary, if it was taken
     on the kernel source as it stands now (else None)."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
-        with open(KERNEL_SRC, "rb") as fh:
-            digest = hashlib.sha256(fh.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in KERNEL_SRCS:
+            with open(path, "rb") as fh:
+                h.update(fh.read())
+        digest = h.hexdigest()
     except (OSError, ValueError):
         return None
     entry = rec.get("workloads", {}).get(workload_name)
-    if entry is None or rec.get("decode_mfma_sha256") != digest:
+    if entry is None or rec.get("decode_kernel_sources_sha256") != digest:
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -307,6 +356,9 @@ def main():
                                    "decode_kernel_gbs": r["decode_kernel_gbs"],
                                    "decode_kernel_frac_of_peak": r["decode_kernel_gbs"] / HBM_PEAK_GBS,
                                    "traffic": traffic_for_current_kernel(w.case.name)}
+            if w.case.shards > 1 and not w.case.paged:
+                others[w.case.name]["per_device_share"] = time_shard_calls(w, args.extra_steps, args.warmup,
+                                                                           not args.no_flush)
             log(f"workload {cfg}: {json.dumps(others[w.case.name])}")
             del w
             torch.cuda.empty_cache()
