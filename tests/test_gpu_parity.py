@@ -28,6 +28,9 @@ SMALL = [
                                transform="wht", extra_pages=5), {}),
     ("g4_h64_contig", dict(batch=3, heads=64, shards=4, lens=[1500, 65, 31], channel_sigma=0.5), {}),
     ("g4_h64_paged", dict(batch=2, heads=64, shards=4, lens=[513, 2000], paged=True, page_size=64), dict(chunk_tokens=256)),
+    ("g4_h128_contig", dict(batch=2, heads=128, shards=4, lens=[900, 70]), {}),
+    ("g4_h128_paged32", dict(batch=2, heads=128, shards=4, lens=[1300, 33], paged=True, page_size=32), {}),
+    ("g4_h32_paged8", dict(batch=3, heads=32, shards=4, lens=[400, 9, 64], paged=True, page_size=8), {}),
     ("g2_h32_paged_wht_chunk64", dict(batch=3, heads=32, shards=2, lens=[900, 100, 5], paged=True, page_size=16,
                                       transform="wht"), dict(chunk_tokens=64)),
     ("g1_h96_paged", dict(batch=2, heads=96, shards=1, lens=[300, 41], paged=True, page_size=32), {}),
