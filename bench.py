@@ -17,7 +17,9 @@ write-back then competes with the timed kernel's reads.
 Prints ONE JSON line.  The headline workload is the DeepSeek-V3-shaped exact MLA
 decode (G = 1, batch 32, 128 heads, latent 512 + rope 64, context 4096, bf16);
 the other workloads (TPLA G = 2 / G = 4 at 32K context, paged + Hadamard with
-ragged contexts) are reported in "workloads" unless --headline-only is given.
+ragged contexts) are reported in "workloads" unless --headline-only is given; the
+contiguous TPLA workloads also carry "per_device_share": the call of one shard (what one
+of G devices would read and compute) and the G = 1 call over the same cache.
 """
 
 from __future__ import annotations
