@@ -248,6 +248,43 @@ def time_shard_calls(w: Workload, steps: int, warmup: int, flush: bool):
     return res
 
 
+def streaming_bandwidth(steps: int = 10):
+    """What plain streaming reaches on this card with the runtime's own kernels: a
+    device-to-device copy of 1 GiB (1 GiB read plus 1 GiB written), and a full reduction of a
+    1 GiB buffer (1 GiB read), each timed with events around it.  Neither kernel is tuned for
+    the card, so these are reference points, not ceilings."""
+    import torch
+
+    buf = _flush_buffer()
+    buf.sum()
+    torch.cuda.synchronize()
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in rev:
+        e[0].record()
+        buf.sum()
+        e[1].record()
+    torch.cuda.synchronize()
+    read_ms = statistics.median(e[0].elapsed_time(e[1]) for e in rev)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        dst.copy_(src)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = statistics.median(e[0].elapsed_time(e[1]) for e in ev)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_gbs": 2 * n / (ms * 1e-3) / 1e9, "copy_ms_median": ms,
+            "read_gbs": buf.numel() * 4 / (read_ms * 1e-3) / 1e9, "read_ms_median": read_ms,
+            "what": "torch device-to-device copy of 1 GiB (read + write) and torch sum of 1 GiB (read)"}
+
+
 def traffic_for_current_kernel(workload_name: str):
     """HBM bytes per decode-kernel launch from the committed counter summary, if it was taken
     on the kernel source as it stands now (else None)."""
@@ -365,6 +402,8 @@ def main():
             del w
             torch.cuda.empty_cache()
         line["workloads"] = others
+    if not args.headline_only:
+        line["achievable_streaming"] = streaming_bandwidth()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_case)
     print(json.dumps(line), flush=True)
