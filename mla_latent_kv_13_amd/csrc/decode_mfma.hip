@@ -1,7 +1,9 @@
 // bf16 split-K TPLA decode on the gfx950 matrix cores.
 //
-// Work unit: one workgroup = (token chunk, sequence b, shard s, group of 32*HB heads).  It streams
-// the chunk's cache rows of that shard -- the latent slice [s*W, (s+1)*W) and the whole rope key,
+// Work unit: one workgroup = (token chunk of sequence b -- or, with the balanced schedule, an
+// equal share of all the batch's tiles, one segment per sequence it touches --, shard s, group of
+// 32*HB heads).  It streams the segment's cache rows of that shard -- the latent slice
+// [s*W, (s+1)*W) and the whole rope key,
 // the per-device share of the TPLA review page (320 = 256 + 64 values per token at two shards) --
 // from HBM straight into a ring of ST LDS tiles of 32 tokens with global_load_lds_dwordx4 (no
 // register staging), keeping ST-1 tiles in flight per workgroup so that enough bytes are
@@ -12,6 +14,8 @@
 // with the value tile read transposed out of LDS by ds_read_b64_tr_b16.  With KS = 2 the two waves
 // of a pair split the key width for S (exchanging fp32 partial logits through LDS) and the value
 // columns for O, which halves the registers each wave needs for the wide single-shard case.
+// One wave per SIMD, except at W = 128 with two or more head blocks, where a wave fits in half the
+// register file and two share each SIMD (see waves_per_simd).
 // The chunk's normalised output and log-sum-exp go to the workspace and the merge kernel combines
 // chunks exactly (feature request on latent-cache sharding, "Directions under investigation":
 // sequence split plus log-sum-exp merge).  The slice softmax is plain, with the same scale on
