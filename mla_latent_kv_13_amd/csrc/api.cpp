@@ -112,19 +112,24 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
       ct = static_cast<int>(std::min<int64_t>(round_up(span, 64), 1024));
     }
   }
-  if (plan->kernel == 1 && ct > 2048) return fail(TPLA_ERR_UNSUPPORTED, "generic kernel chunk_tokens must be <= 2048");
-  if (plan->kernel == 2 && d->max_pages_per_seq > 0) {
-    // a chunk's block-table entries are staged in LDS
-    const int max_ct = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(tpla::mfma_max_chunk_pages() - 1) * d->page_size, 1 << 30));
-    if (ct > max_ct) {
-      if (opts && opts->chunk_tokens) return fail(TPLA_ERR_UNSUPPORTED, "chunk_tokens spans more cache pages than the kernel stages");
-      ct = std::max(64, max_ct / 64 * 64);
-    }
+  // Longest chunk each kernel takes: the generic kernel keeps a chunk's logits in LDS; the MFMA
+  // kernel on a paged cache stages a chunk's block-table entries there.
+  int max_ct = 1 << 30;
+  if (plan->kernel == 1) max_ct = 2048;
+  if (plan->kernel == 2 && d->max_pages_per_seq > 0)
+    max_ct = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(tpla::mfma_max_chunk_pages() - 1) * d->page_size, 1 << 30));
+  max_ct = std::max(64, max_ct / 64 * 64);
+  if (ct > max_ct) {
+    if (opts && opts->chunk_tokens)
+      return fail(TPLA_ERR_UNSUPPORTED, plan->kernel == 1 ? "generic kernel chunk_tokens must be <= 2048"
+                                                           : "chunk_tokens spans more cache pages than the kernel stages");
+    ct = max_ct;
   }
   int nc = (span + ct - 1) / ct;
   if (nc > kMaxChunksMerge) {
+    // Past this many chunks, chunks grow (up to the kernel's limit) rather than the partials.
     if (opts && opts->chunk_tokens) return fail(TPLA_ERR_UNSUPPORTED, "more than %d chunks per sequence", kMaxChunksMerge);
-    ct = static_cast<int>(round_up((span + kMaxChunksMerge - 1) / kMaxChunksMerge, 64));
+    ct = static_cast<int>(std::min<int64_t>(round_up((span + kMaxChunksMerge - 1) / kMaxChunksMerge, 64), max_ct));
     nc = (span + ct - 1) / ct;
   }
   plan->chunk_tokens = ct;

@@ -571,15 +571,15 @@ hipError_t launch_one(const DecodeLaunch& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  const int units = a.sched == 1 ? a.workers : a.num_chunks * a.batch;
+  const int64_t units = a.sched == 1 ? a.workers : static_cast<int64_t>(a.num_chunks) * a.batch;
   const int members = a.shard_count * (a.heads / (32 * HB));
-  const int64_t blocks = static_cast<int64_t>((units + 7) / 8) * 8 * members;
+  const int64_t blocks = (units + 7) / 8 * 8 * members;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   int page_shift = -1;
   if (LAYOUT != 0 && (a.page_size & (a.page_size - 1)) == 0) page_shift = __builtin_ctz(a.page_size);
   const float scale_log2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(C::THREADS), C::LDS_BYTES, stream, a, scale_log2,
-                     units, members, page_shift);
+                     static_cast<int>(units), members, page_shift);
   return hipGetLastError();
 }
 

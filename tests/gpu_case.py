@@ -59,8 +59,9 @@ class DeviceCase:
                                            shard_count=shard_count, **kw)
 
 
-def oracle_decode(case: inputs.Case, seqs=None, shard_begin=0, shard_count=None):
-    """Oracle output for sequences `seqs` (all by default) on a compact contiguous pool built
+def oracle_decode(case: inputs.Case, seqs=None, shard_begin=0, shard_count=None, heads=None):
+    """Oracle output for sequences `seqs` (all by default) and query heads `heads` (all by
+    default; heads are independent, so a subset is exact) on a compact contiguous pool built
     from the case's raw rows (the oracle's own append builds rotated caches)."""
     if seqs is None:
         seqs = list(range(case.batch))
@@ -83,6 +84,8 @@ def oracle_decode(case: inputs.Case, seqs=None, shard_begin=0, shard_count=None)
                                           case.transform, case.dtype)
     q_lat = inputs.stored_to_f64(case.q_lat, case.dtype)[seqs]
     q_rope = inputs.stored_to_f64(case.q_rope, case.dtype)[seqs]
+    if heads is not None:
+        q_lat, q_rope = q_lat[:, list(heads)], q_rope[:, list(heads)]
     return oracle.tpla_decode_sharded(pool, None, lens, q_lat, q_rope, float(np.float32(case.scale)), case.shards,
                                       shard_begin, shard_count, transform=case.transform)
 

@@ -56,6 +56,28 @@ def test_workspace_size_host_only(lib):
     assert binding.workspace_size(DSV3, 16, 128, 2, 2, 32768, schedule="balanced") == n
 
 
+def _ru(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_size_long_contexts(lib):
+    """Past 4096 chunks a sequence's chunks grow, but never beyond what the kernel takes: 960
+    tokens for the MFMA kernel on 1-row pages (1021 staged pages), 2048 for the generic kernel."""
+    g, w = 2, 256
+    paged1 = binding.Desc("bf16", 512, 64, 1, 8_000_000, 8_000_000, "identity")
+    nc, heads = -(-8_000_000 // 960), 128
+    assert binding.workspace_size(paged1, 1, heads, g, g, 8_000_000, schedule="chunked") == \
+        _ru(nc * g * heads * w * 4) + _ru(nc * g * heads * 4)
+    f32 = binding.Desc("f32", 512, 64, 16_000_000, 1, 0, "identity")
+    nc, heads = -(-16_000_000 // 2048), 4
+    assert binding.workspace_size(f32, 1, heads, g, g, 16_000_000) == _ru(nc * g * heads * w * 4) + _ru(nc * g * heads * 4)
+    # an explicit chunk length is taken as given or refused
+    with pytest.raises(binding.TplaError, match="UNSUPPORTED"):
+        binding.workspace_size(f32, 1, heads, g, g, 16_000_000, chunk_tokens=4096)
+    with pytest.raises(binding.TplaError, match="UNSUPPORTED"):
+        binding.workspace_size(paged1, 1, 128, g, g, 8_000_000, chunk_tokens=1024, schedule="chunked")
+
+
 @pytest.mark.parametrize("kw,msg", [
     (dict(num_shards=3), "INVALID_ARGUMENT"),            # 3 does not divide 512
     (dict(num_shards=2, shard_count=3), "INVALID_ARGUMENT"),

@@ -224,3 +224,65 @@ def test_full_size_workloads_sampled(cfg):
     rel, mx = assert_parity(out_np[seqs], ref, "bf16", f"config {cfg}")
     assert_lse(_np(lse)[seqs], ref_lse, "bf16", f"config {cfg}", case.transform)
     _say(f"config {cfg}: rel L2 {rel:.2e} max {mx:.2e}")
+
+
+# Long contexts: a 17-token sequence beside one of 1,000,003 tokens (a ragged last tile).  In
+# the contiguous layout the long sequence owns page 1 of the pool, so its rows lie 1.15 to 2.3 GB
+# into it (past 2^31 bytes from token 864,133 on); with 1-row pages every token sits on a page of
+# its own and the balanced schedule needs over a thousand workers.  Four tokens of the long
+# sequence are replaced by one head's own query, which then dominates that head's softmax: a
+# lost, doubled or misplaced row moves that head's output by far more than the tolerance.
+LONG_LENS = [17, 1_000_003]
+LONG_PLANTS = [(0, 0), (524_287, 38), (900_000, 63), (1_000_002, 13)]  # (token, head)
+LONG_HEADS = [0, 7, 13, 38, 63]
+LONG_LAYOUTS = {"contig": dict(paged=False), "paged64": dict(paged=True, page_size=64),
+                "paged1": dict(paged=True, page_size=1)}
+LONG = [("contig", 1, {}), ("contig", 2, {}), ("contig", 4, {}), ("contig", 2, dict(schedule="balanced")),
+        ("contig", 2, dict(kernel="generic")), ("paged64", 2, {}), ("paged64", 4, dict(schedule="chunked")),
+        ("paged1", 2, {})]
+_long_cache = {}
+
+
+def _plant(case, b, picks):
+    """Set token t of sequence b to head h's own query (same stored type), for (t, h) in picks."""
+    start = int(case.seq_lens[:b].astype(np.int64).sum())
+    flat = case.pool.reshape(-1, case.width)
+    for t, h in picks:
+        i = start + t
+        case.rows[i, :case.d_latent] = case.q_lat[b, h]
+        case.rows[i, case.d_latent:] = case.q_rope[b, h]
+        flat[case.slots[i]] = case.rows[i]
+
+
+def _long_case(layout):
+    if layout not in _long_cache:
+        _long_cache.clear()  # one layout's host and device copies at a time
+        torch.cuda.empty_cache()
+        _say(f"long {layout}: generating")
+        case = inputs.make_case(1234, batch=2, heads=64, d_latent=512, d_rope=64, shards=2, lens=LONG_LENS,
+                                scale=1.0 / np.sqrt(192), name=f"long-{layout}", **LONG_LAYOUTS[layout])
+        _plant(case, 1, LONG_PLANTS)
+        _long_cache[layout] = (case, DeviceCase(case))
+    return _long_cache[layout]
+
+
+@pytest.mark.parametrize("layout,g,dkw", LONG, ids=[f"{l}_g{g}_{'_'.join(d.values()) or 'auto'}" for l, g, d in LONG])
+def test_million_token_context_sampled(layout, g, dkw):
+    import dataclasses
+    base, dc = _long_case(layout)
+    case = dataclasses.replace(base, shards=g)
+    dc.case = case
+    _say(f"long {layout} G={g} {dkw}: decoding")
+    out, lse = dc.decode(**dkw)
+    torch.cuda.synchronize()
+    out_np, lse_np = _np(out), _np(lse)
+    assert np.all(np.isfinite(out_np)) and np.all(np.isfinite(lse_np))
+    _say(f"long {layout} G={g}: oracle")
+    ref, ref_lse = oracle_decode(case, [0])
+    assert_parity(out_np[[0]], ref, "bf16", f"long {layout} G={g} short sequence")
+    assert_lse(lse_np[[0]], ref_lse, "bf16", f"long {layout} G={g} short sequence")
+    ref, ref_lse = oracle_decode(case, [1], heads=LONG_HEADS)
+    for k, h in enumerate(LONG_HEADS):
+        rel, mx = assert_parity(out_np[1, h], ref[0, k], "bf16", f"long {layout} G={g} head {h}")
+        _say(f"  head {h}: rel L2 {rel:.2e} max {mx:.2e}")
+    assert_lse(lse_np[1][:, LONG_HEADS], ref_lse[0], "bf16", f"long {layout} G={g} long sequence")
