@@ -11,19 +11,75 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxLatent = 1024;
 
-template <typename T>
+constexpr int kRowsPerBlock = kThreads / 64;  // one wave per appended row
+
+// V elements of T read or written as one aligned access.
+template <typename T, int V>
+struct alignas(sizeof(T) * V) Pack {
+  T v[V];
+};
+
+// One wave per row: lane l holds latent elements V*l .. V*l+V-1 (V = d_latent / 64, or 1 with
+// lanes >= d_latent idle), so element e = V*lane + r.  Butterflies on pairs (e, e + span), span
+// increasing: within a lane's registers while span < V, then across lanes (lane bit span / V);
+// then the 1/sqrt(d_latent) scale.
+template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void append_wht_kernel(T* __restrict__ cache, const T* __restrict__ rows,
-                                                               const int64_t* __restrict__ slots, int d_latent,
-                                                               int d_rope) {
-  __shared__ float x[kMaxLatent];
-  const int64_t i = blockIdx.x;
+                                                               const int64_t* __restrict__ slots, int64_t n,
+                                                               int d_latent, int d_rope) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  if (i >= n) return;
   const int64_t D = d_latent + d_rope;
   const T* src = rows + i * D;
   T* dst = cache + slots[i] * D;
-  for (int j = threadIdx.x; j < d_latent; j += kThreads) x[j] = load_as_f32(src + j);
-  block_fwht(x, d_latent);
-  for (int j = threadIdx.x; j < d_latent; j += kThreads) dst[j] = store_from_f32<T>(x[j]);
-  for (int j = threadIdx.x; j < d_rope; j += kThreads) dst[d_latent + j] = src[d_latent + j];
+  const int lanes = d_latent / V;  // lanes holding latent elements (<= 64)
+  const bool on = lane < lanes;
+  Pack<T, V> p = on ? reinterpret_cast<const Pack<T, V>*>(src)[lane] : Pack<T, V>{};
+  float x[V];
+#pragma unroll
+  for (int r = 0; r < V; ++r) x[r] = load_as_f32(&p.v[r]);
+#pragma unroll
+  for (int span = 1; span < V; span <<= 1) {
+#pragma unroll
+    for (int r = 0; r < V; ++r) {
+      if ((r & span) == 0) {
+        const float u = x[r], w = x[r + span];
+        x[r] = u + w;
+        x[r + span] = u - w;
+      }
+    }
+  }
+  for (int ls = 1; ls < lanes; ls <<= 1) {
+#pragma unroll
+    for (int r = 0; r < V; ++r) {
+      const float other = __shfl_xor(x[r], ls);
+      x[r] = (lane & ls) ? other - x[r] : x[r] + other;
+    }
+  }
+  const float norm = 1.0f / sqrtf(static_cast<float>(d_latent));
+#pragma unroll
+  for (int r = 0; r < V; ++r) p.v[r] = store_from_f32<T>(x[r] * norm);
+  if (on) reinterpret_cast<Pack<T, V>*>(dst)[lane] = p;
+  // rope key: unchanged, 16 bytes per lane (d_latent and d_rope elements are multiples of 16 bytes)
+  const int pieces = d_rope * static_cast<int>(sizeof(T)) / 16;
+  for (int k = lane; k < pieces; k += 64)
+    reinterpret_cast<uint4*>(dst + d_latent)[k] = reinterpret_cast<const uint4*>(src + d_latent)[k];
+}
+
+template <typename T>
+hipError_t launch_wht(T* cache, const T* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
+                      hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + kRowsPerBlock - 1) / kRowsPerBlock));
+  switch (d_latent <= 64 ? 1 : d_latent / 64) {
+    case 1: hipLaunchKernelGGL((append_wht_kernel<T, 1>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
+    case 2: hipLaunchKernelGGL((append_wht_kernel<T, 2>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
+    case 4: hipLaunchKernelGGL((append_wht_kernel<T, 4>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
+    case 8: hipLaunchKernelGGL((append_wht_kernel<T, 8>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
+    case 16: hipLaunchKernelGGL((append_wht_kernel<T, 16>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // Plain copy of whole rows in 16-byte pieces (row bytes are a multiple of 16).
@@ -49,13 +105,13 @@ hipError_t launch_append(void* cache, const void* rows, const int64_t* slots, in
   if (n == 0) return hipSuccess;
   const int elem = dtype == 0 ? 4 : 2;
   if (wht) {
-    if (d_latent > kMaxLatent || n > 0x7fffffffLL) return hipErrorInvalidValue;
+    // a power of two up to 1024 (checked with the descriptor); rows in whole 16-byte pieces
+    if (d_latent > kMaxLatent || (d_latent & (d_latent - 1)) != 0 || n > 0x7fffffffLL) return hipErrorInvalidValue;
+    if ((d_latent * elem) % 16 != 0 || (d_rope * elem) % 16 != 0) return hipErrorInvalidValue;
     if (dtype == 0)
-      hipLaunchKernelGGL(append_wht_kernel<float>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream,
-                         static_cast<float*>(cache), static_cast<const float*>(rows), slots, d_latent, d_rope);
-    else
-      hipLaunchKernelGGL(append_wht_kernel<uint16_t>, dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream,
-                         static_cast<uint16_t*>(cache), static_cast<const uint16_t*>(rows), slots, d_latent, d_rope);
+      return launch_wht(static_cast<float*>(cache), static_cast<const float*>(rows), slots, n, d_latent, d_rope, stream);
+    return launch_wht(static_cast<uint16_t*>(cache), static_cast<const uint16_t*>(rows), slots, n, d_latent, d_rope,
+                      stream);
   } else {
     const int row_bytes = (d_latent + d_rope) * elem;
     const int64_t total = n * (row_bytes / 16);

@@ -68,7 +68,113 @@ struct Vec<1> {
   static __device__ __forceinline__ void fma(float w, const T& v, T& acc) { acc = fmaf(w, v, acc); }
 };
 
-template <int V>
+// Lane v's value from another lane of its row of 16 (DPP; every lane reads a valid source).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Maximum (MAX) or sum over aligned groups of gw lanes (gw a power of two <= 64); every lane of a
+// group receives its group's result.  Below 16 lanes: DPP swaps of lane pairs (lane ^ 1, lane ^ 2),
+// then of the two quads of each 8 and the two halves of each 16 (mirrors).
+template <bool MAX>
+__device__ __forceinline__ float group_reduce(float v, int gw) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if (gw > 1) v = op(v, dpp_mov<0xb1>(v));   // quad_perm(1, 0, 3, 2)
+  if (gw > 2) v = op(v, dpp_mov<0x4e>(v));   // quad_perm(2, 3, 0, 1)
+  if (gw > 4) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
+  if (gw > 8) v = op(v, dpp_mov<0x140>(v));  // row_mirror
+  if (gw > 16) v = op(v, __shfl_xor(v, 16));
+  if (gw > 32) v = op(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Merge of one (sequence, head) for nb computed shards from s0, in a single pass.  Shard s0 + q's
+// partials are rows q * n2 + k, k < n2 (n2 = a power of two >= the slots per shard nr and >= P;
+// rows k >= nr are padding).  A shard's arithmetic does not depend on s0 or nb.  A
+// load step covers P rows (lane group g = lane / (64 / P) takes row step * P + g, P > 1 when a
+// slice row is at most 32 float4) and E float4 per lane of each (E = 2 when it is 65..128
+// float4); S steps.  Lane j also holds row j's log-sum-exp, so each shard's maximum and sum are
+// reductions over an aligned group of n2 lanes, all shards at once.  Every load is issued before
+// any value is needed (no branch around a load: rows and vectors past the end are clamped to
+// valid ones and never used), so the wave waits on memory once; the number of slots holding
+// tokens, nv <= nr, comes from get_nv() after the loads.
+template <int E, int P, int S, typename NV>
+__device__ __forceinline__ void merge_one_pass(const MergeLaunch& a, int b, int h, int lane, int64_t slot0, int nr,
+                                               int lg2, int s0, int nb, NV get_nv, float* y) {
+  constexpr int GW = 64 / P;  // lanes per row of a load step
+  const int n2 = 1 << lg2, sc = a.shard_count, nvec = a.w / 4;
+  const int64_t heads = a.heads;
+  const int g = lane / GW, c = lane % GW;
+  auto part_row = [&](int j) {  // partial row of row j (padding rows read slot nr - 1)
+    const int sl = s0 + (j >> lg2), k = min(j & (n2 - 1), nr - 1);
+    return ((slot0 + k) * sc + sl) * heads + h;
+  };
+  const int R = nb * n2;
+  const float lse_raw = a.part_lse[part_row(min(lane, R - 1))];
+  float4 v[S][E];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const float4* src = reinterpret_cast<const float4*>(a.part_o + part_row(min(i * P + g, R - 1)) * a.w);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[i][e] = src[min(c + 64 * e, nvec - 1)];
+  }
+  const int nv = get_nv();
+  const int kl = lane & (n2 - 1);
+  const bool live = lane < R && kl < nv;
+  const float lse_l = live ? lse_raw : -INFINITY;
+  const float M = group_reduce<true>(lse_l, n2);
+  const float Z = group_reduce<false>(live ? expf(lse_l - M) : 0.f, n2);
+  const float wl = live ? expf(lse_l - M) * (1.0f / Z) : 0.f;
+  if (a.lse != nullptr && kl == 0 && lane < R)
+    a.lse[(static_cast<int64_t>(b) * sc + s0 + (lane >> lg2)) * heads + h] = nv > 0 ? M + logf(Z) : -INFINITY;
+  float4 acc[E];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int j0 = i * P;  // first row of this step (uniform)
+    if (j0 < R) {
+      if ((j0 & (n2 - 1)) == 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j0));
+#pragma unroll
+      for (int gg = 1; gg < P; ++gg) {
+        const float wg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j0 + gg));
+        wt = g == gg ? wg : wt;
+      }
+      if (((j0 + g) & (n2 - 1)) < nv) {  // rows without tokens may hold stale values: never multiplied
+#pragma unroll
+        for (int e = 0; e < E; ++e) Vec<4>::fma(wt, v[i][e], acc[e]);
+      }
+      if (((j0 + P) & (n2 - 1)) == 0) {  // last step of shard j0 / n2: add the P groups, store
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+#pragma unroll
+          for (int off = GW; off < 64; off <<= 1) {
+            acc[e].x += __shfl_xor(acc[e].x, off);
+            acc[e].y += __shfl_xor(acc[e].y, off);
+            acc[e].z += __shfl_xor(acc[e].z, off);
+            acc[e].w += __shfl_xor(acc[e].w, off);
+          }
+        }
+        float4* yd = reinterpret_cast<float4*>(y + (a.shard_begin + s0 + (j0 >> lg2)) * a.w);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (g == 0 && c + 64 * e < nvec) yd[c + 64 * e] = acc[e];
+      }
+    }
+  }
+}
+
+// Slots per shard padded to a power of two no less than p: log2.
+__device__ __forceinline__ int pad_log2(int nr, int p) {
+  const int m = max(nr, p);
+  return 32 - __clz(m - 1);
+}
+
+// E > 0: the one-pass path (E, P, S as above) is compiled in for waves whose partials fit it.
+template <int V, int E, int P, int S>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
   typedef typename Vec<V>::T vec_t;
   __shared__ __attribute__((aligned(16))) float ybuf[kMergeWaves][kMaxLatent];
@@ -76,6 +182,25 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
   const int h = blockIdx.x * kMergeWaves + wv, b = blockIdx.y;
   if (h >= a.heads) return;  // the rest of this kernel is wave-local
   float* y = ybuf[wv];
+  const int lo = a.shard_begin * a.w, hi = lo + a.shard_count * a.w;
+  for (int j = lane; j < a.d_latent; j += 64)
+    if (j < lo || j >= hi) y[j] = 0.f;  // latent columns of shards that were not computed
+  if constexpr (E > 0) {
+    // chunked schedule: the loads of every chunk slot go out before the context length arrives
+    if (a.sched == 0) {
+      const int lg2 = pad_log2(a.num_chunks, P);
+      if ((1 << lg2) <= min(64, S * P)) {
+        const int per = min(64, S * P) >> lg2;  // shards per pass
+        for (int s0 = 0; s0 < a.shard_count; s0 += per)
+          merge_one_pass<E, P, S>(a, b, h, lane, static_cast<int64_t>(b) * a.num_chunks, a.num_chunks, lg2, s0,
+                                  min(per, a.shard_count - s0), [&] {
+                                    return (a.seq_lens[b] + a.chunk_tokens - 1) / a.chunk_tokens;
+                                  }, y);
+        goto rows_done;
+      }
+    }
+  }
+  {
   // Partials of sequence b: nv consecutive slots from slot0 (chunks holding tokens, or the
   // workers whose tile share meets the sequence under the balanced schedule).
   int nv;
@@ -93,9 +218,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
     nv = p1 > p0 ? static_cast<int>(worker_of(p1 - 1) - worker_of(p0) + 1) : 0;
     slot0 = p1 > p0 ? b + worker_of(p0) : 0;
   }
-  const int lo = a.shard_begin * a.w, hi = lo + a.shard_count * a.w;
-  for (int j = lane; j < a.d_latent; j += 64)
-    if (j < lo || j >= hi) y[j] = 0.f;  // latent columns of shards that were not computed
+  if constexpr (E > 0) {
+    const int lg2 = pad_log2(max(nv, 1), P);
+    if ((1 << lg2) <= min(64, S * P)) {
+      const int per = min(64, S * P) >> lg2;
+      for (int s0 = 0; s0 < a.shard_count; s0 += per)
+        merge_one_pass<E, P, S>(a, b, h, lane, slot0, max(nv, 1), lg2, s0, min(per, a.shard_count - s0),
+                                [&] { return nv; }, y);
+      goto rows_done;
+    }
+  }
 
   const int64_t stride = static_cast<int64_t>(a.shard_count) * a.heads;  // partial rows between chunks
   const int wv_cols = a.w / V;                                              // vectors per slice row
@@ -143,6 +275,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
     if (a.lse != nullptr && lane == 0)
       a.lse[(static_cast<int64_t>(b) * a.shard_count + sl) * a.heads + h] = nv > 0 ? M + logf(Z) : -INFINITY;
   }
+  }
+rows_done:
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // this wave's LDS row is complete
   __builtin_amdgcn_wave_barrier();
 
@@ -161,19 +295,29 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
   }
 }
 
+// One wave per query row, four rows per block: the row sits in registers (x[r] = q[lane + 64 r])
+// and is rotated by the same butterflies as the merge's output rotation.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void rotate_query_kernel(const T* __restrict__ q, int d_latent, void* dst,
-                                                                 int dst_f32) {
-  __shared__ float x[kMaxLatent];
-  const int64_t r = blockIdx.x;
-  for (int j = threadIdx.x; j < d_latent; j += kThreads) x[j] = load_as_f32(q + r * d_latent + j);
-  block_fwht(x, d_latent);
-  if (dst_f32) {
-    float* o = static_cast<float*>(dst) + r * d_latent;
-    for (int j = threadIdx.x; j < d_latent; j += kThreads) o[j] = x[j];
-  } else {
-    uint16_t* o = static_cast<uint16_t*>(dst) + r * d_latent;
-    for (int j = threadIdx.x; j < d_latent; j += kThreads) o[j] = f32_to_bf16(x[j]);
+__global__ __launch_bounds__(kThreads) void rotate_query_kernel(const T* __restrict__ q, int rows, int d_latent,
+                                                                 void* dst, int dst_f32) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float x[kMaxLatent / 64];
+#pragma unroll
+  for (int i = 0; i < kMaxLatent / 64; ++i) {
+    const int j = lane + 64 * i;
+    x[i] = j < d_latent ? load_as_f32(q + r * d_latent + j) : 0.f;
+  }
+  wave_fwht(x, d_latent, lane);
+#pragma unroll
+  for (int i = 0; i < kMaxLatent / 64; ++i) {
+    const int j = lane + 64 * i;
+    if (j >= d_latent) continue;
+    if (dst_f32)
+      static_cast<float*>(dst)[r * d_latent + j] = x[i];
+    else
+      static_cast<uint16_t*>(dst)[r * d_latent + j] = f32_to_bf16(x[i]);
   }
 }
 
@@ -213,22 +357,41 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
   if (a.d_latent > kMaxLatent) return hipErrorInvalidValue;
   if (a.wht && (a.d_latent & (a.d_latent - 1)) != 0) return hipErrorInvalidValue;
   const dim3 grid((a.heads + kMergeWaves - 1) / kMergeWaves, a.batch);
-  if (a.w % 4 == 0)
-    hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(kThreads), 0, stream, a);
+  // One-pass shape: float4 per lane per row (E) or rows per load step (P) from the slice width;
+  // steps S: the fewest of 4, 8 and 16 / E that hold every chunk row of all shards under the
+  // chunked schedule (else 16 / E, shards in several passes), and 16 / E under the balanced
+  // schedule, where the rows per sequence vary.
+  const int nvec = a.w / 4;
+  const int e = a.w % 4 != 0 || nvec > 128 ? 0 : (nvec > 64 ? 2 : 1);
+  const int pr = nvec > 32 ? 1 : (nvec > 16 ? 2 : 4);
+  int steps = 16 / max(e, 1);
+  if (a.sched == 0) {
+    int n2 = pr;
+    while (n2 < a.num_chunks) n2 <<= 1;
+    const int need = a.shard_count * n2 / pr;
+    steps = need <= 4 ? 4 : (need <= 8 ? 8 : steps);
+  }
+  using K = void (*)(MergeLaunch);
+  K kern;
+  if (e == 0) kern = a.w % 4 == 0 ? merge_kernel<4, 0, 1, 1> : merge_kernel<1, 0, 1, 1>;
+  else if (e == 2) kern = steps == 4 ? merge_kernel<4, 2, 1, 4> : merge_kernel<4, 2, 1, 8>;
+  else if (pr == 1) kern = steps == 4 ? merge_kernel<4, 1, 1, 4> : steps == 8 ? merge_kernel<4, 1, 1, 8> : merge_kernel<4, 1, 1, 16>;
+  else if (pr == 2) kern = steps == 4 ? merge_kernel<4, 1, 2, 4> : steps == 8 ? merge_kernel<4, 1, 2, 8> : merge_kernel<4, 1, 2, 16>;
+  else kern = steps == 4 ? merge_kernel<4, 1, 4, 4> : steps == 8 ? merge_kernel<4, 1, 4, 8> : merge_kernel<4, 1, 4, 16>;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_latent, void* dst, int dst_f32,
                                hipStream_t stream) {
   if (d_latent > kMaxLatent) return hipErrorInvalidValue;
+  const dim3 grid((rows + kMergeWaves - 1) / kMergeWaves);
   if (dtype == 0)
-    hipLaunchKernelGGL(rotate_query_kernel<float>, dim3(rows), dim3(kThreads), 0, stream,
-                       static_cast<const float*>(q_lat), d_latent, dst, dst_f32);
+    hipLaunchKernelGGL(rotate_query_kernel<float>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const float*>(q_lat), rows, d_latent, dst, dst_f32);
   else
-    hipLaunchKernelGGL(rotate_query_kernel<uint16_t>, dim3(rows), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q_lat), d_latent, dst, dst_f32);
+    hipLaunchKernelGGL(rotate_query_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q_lat), rows, d_latent, dst, dst_f32);
   return hipGetLastError();
 }
 
