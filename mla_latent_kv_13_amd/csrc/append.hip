@@ -13,16 +13,8 @@ constexpr int kMaxLatent = 1024;
 
 constexpr int kRowsPerBlock = kThreads / 64;  // one wave per appended row
 
-// V elements of T read or written as one aligned access.
-template <typename T, int V>
-struct alignas(sizeof(T) * V) Pack {
-  T v[V];
-};
-
 // One wave per row: lane l holds latent elements V*l .. V*l+V-1 (V = d_latent / 64, or 1 with
-// lanes >= d_latent idle), so element e = V*lane + r.  Butterflies on pairs (e, e + span), span
-// increasing: within a lane's registers while span < V, then across lanes (lane bit span / V);
-// then the 1/sqrt(d_latent) scale.
+// lanes >= d_latent idle), rotated in registers.
 template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void append_wht_kernel(T* __restrict__ cache, const T* __restrict__ rows,
                                                                const int64_t* __restrict__ slots, int64_t n,
@@ -39,27 +31,9 @@ __global__ __launch_bounds__(kThreads) void append_wht_kernel(T* __restrict__ ca
   float x[V];
 #pragma unroll
   for (int r = 0; r < V; ++r) x[r] = load_as_f32(&p.v[r]);
+  wave_wht(x, d_latent, lane);
 #pragma unroll
-  for (int span = 1; span < V; span <<= 1) {
-#pragma unroll
-    for (int r = 0; r < V; ++r) {
-      if ((r & span) == 0) {
-        const float u = x[r], w = x[r + span];
-        x[r] = u + w;
-        x[r + span] = u - w;
-      }
-    }
-  }
-  for (int ls = 1; ls < lanes; ls <<= 1) {
-#pragma unroll
-    for (int r = 0; r < V; ++r) {
-      const float other = __shfl_xor(x[r], ls);
-      x[r] = (lane & ls) ? other - x[r] : x[r] + other;
-    }
-  }
-  const float norm = 1.0f / sqrtf(static_cast<float>(d_latent));
-#pragma unroll
-  for (int r = 0; r < V; ++r) p.v[r] = store_from_f32<T>(x[r] * norm);
+  for (int r = 0; r < V; ++r) p.v[r] = store_from_f32<T>(x[r]);
   if (on) reinterpret_cast<Pack<T, V>*>(dst)[lane] = p;
   // rope key: unchanged, 16 bytes per lane (d_latent and d_rope elements are multiples of 16 bytes)
   const int pieces = d_rope * static_cast<int>(sizeof(T)) / 16;

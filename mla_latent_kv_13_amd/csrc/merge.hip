@@ -19,32 +19,13 @@ constexpr int kThreads = 256;
 constexpr int kMaxLatent = 1024;
 constexpr int kMergeWaves = kThreads / 64;  // one (sequence, head) per wave
 
-// In-place orthonormal Walsh-Hadamard transform (Sylvester order) of the n values a wave holds as
-// x[r] = v[lane + 64 r] (n a power of two <= 1024; lanes >= n idle when n < 64): radix-2 butterflies
-// on pairs (i, i + span), across lanes for span < 64 and across registers above, then 1/sqrt(n).
-__device__ __forceinline__ void wave_fwht(float (&x)[kMaxLatent / 64], int n, int lane) {
-  const int lanes = n < 64 ? n : 64;
-  for (int span = 1; span < lanes; span <<= 1) {
-#pragma unroll
-    for (int r = 0; r < kMaxLatent / 64; ++r) {
-      const float other = __shfl_xor(x[r], span);
-      x[r] = (lane & span) ? other - x[r] : x[r] + other;
-    }
-  }
-  const int regs = n / 64;
-  for (int sr = 1; sr < regs; sr <<= 1) {
-#pragma unroll
-    for (int r = 0; r < kMaxLatent / 64; ++r) {
-      if ((r & sr) == 0 && r + sr < kMaxLatent / 64) {
-        const float u = x[r], v = x[r + sr];
-        x[r] = u + v;
-        x[r + sr] = u - v;
-      }
-    }
-  }
-  const float norm = 1.0f / sqrtf(static_cast<float>(n));
-#pragma unroll
-  for (int r = 0; r < kMaxLatent / 64; ++r) x[r] *= norm;
+// out = H y for the summed latent row y (LDS), V consecutive values per lane.
+template <int V>
+__device__ __forceinline__ void rotate_out(const float* y, float* dst, int n, int lane) {
+  const bool on = lane < n / V;
+  Pack<float, V> p = on ? reinterpret_cast<const Pack<float, V>*>(y)[lane] : Pack<float, V>{};
+  wave_wht(p.v, n, lane);
+  if (on) reinterpret_cast<Pack<float, V>*>(dst)[lane] = p;
 }
 
 // Columns a lane accumulates at once: V = 4 (float4; slice width a multiple of 4) or 1.
@@ -67,12 +48,6 @@ struct Vec<1> {
   static __device__ __forceinline__ T zero() { return 0.f; }
   static __device__ __forceinline__ void fma(float w, const T& v, T& acc) { acc = fmaf(w, v, acc); }
 };
-
-// Lane v's value from another lane of its row of 16 (DPP; every lane reads a valid source).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
 
 // Maximum (MAX) or sum over aligned groups of gw lanes (gw a power of two <= 64); every lane of a
 // group receives its group's result.  Below 16 lanes: DPP swaps of lane pairs (lane ^ 1, lane ^ 2),
@@ -177,7 +152,7 @@ __device__ __forceinline__ int pad_log2(int nr, int p) {
 template <int V, int E, int P, int S>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
   typedef typename Vec<V>::T vec_t;
-  __shared__ __attribute__((aligned(16))) float ybuf[kMergeWaves][kMaxLatent];
+  __shared__ __attribute__((aligned(64))) float ybuf[kMergeWaves][kMaxLatent];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.x * kMergeWaves + wv, b = blockIdx.y;
   if (h >= a.heads) return;  // the rest of this kernel is wave-local
@@ -280,45 +255,60 @@ rows_done:
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // this wave's LDS row is complete
   __builtin_amdgcn_wave_barrier();
 
-  float x[kMaxLatent / 64];
-#pragma unroll
-  for (int r = 0; r < kMaxLatent / 64; ++r) {
-    const int j = lane + 64 * r;
-    x[r] = j < a.d_latent ? y[j] : 0.f;
-  }
-  if (a.wht) wave_fwht(x, a.d_latent, lane);
   float* dst = a.out + (static_cast<int64_t>(b) * a.heads + h) * a.d_latent;
-#pragma unroll
-  for (int r = 0; r < kMaxLatent / 64; ++r) {
-    const int j = lane + 64 * r;
-    if (j < a.d_latent) dst[j] = x[r];
+  if (!a.wht) {
+    for (int j = lane; j < a.d_latent / 4; j += 64)
+      reinterpret_cast<float4*>(dst)[j] = reinterpret_cast<const float4*>(y)[j];
+    return;
+  }
+  switch (a.d_latent <= 64 ? 1 : a.d_latent / 64) {
+    case 1: rotate_out<1>(y, dst, a.d_latent, lane); break;
+    case 2: rotate_out<2>(y, dst, a.d_latent, lane); break;
+    case 4: rotate_out<4>(y, dst, a.d_latent, lane); break;
+    case 8: rotate_out<8>(y, dst, a.d_latent, lane); break;
+    default: rotate_out<16>(y, dst, a.d_latent, lane); break;
   }
 }
 
-// One wave per query row, four rows per block: the row sits in registers (x[r] = q[lane + 64 r])
-// and is rotated by the same butterflies as the merge's output rotation.
-template <typename T>
+// One wave per query row, four rows per block: V consecutive values per lane, rotated in registers.
+template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void rotate_query_kernel(const T* __restrict__ q, int rows, int d_latent,
                                                                  void* dst, int dst_f32) {
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
   if (r >= rows) return;
-  float x[kMaxLatent / 64];
+  const bool on = lane < d_latent / V;
+  const Pack<T, V> p = on ? reinterpret_cast<const Pack<T, V>*>(q + r * d_latent)[lane] : Pack<T, V>{};
+  float x[V];
 #pragma unroll
-  for (int i = 0; i < kMaxLatent / 64; ++i) {
-    const int j = lane + 64 * i;
-    x[i] = j < d_latent ? load_as_f32(q + r * d_latent + j) : 0.f;
-  }
-  wave_fwht(x, d_latent, lane);
+  for (int i = 0; i < V; ++i) x[i] = load_as_f32(&p.v[i]);
+  wave_wht(x, d_latent, lane);
+  if (!on) return;
+  if (dst_f32) {
+    Pack<float, V> o;
 #pragma unroll
-  for (int i = 0; i < kMaxLatent / 64; ++i) {
-    const int j = lane + 64 * i;
-    if (j >= d_latent) continue;
-    if (dst_f32)
-      static_cast<float*>(dst)[r * d_latent + j] = x[i];
-    else
-      static_cast<uint16_t*>(dst)[r * d_latent + j] = f32_to_bf16(x[i]);
+    for (int i = 0; i < V; ++i) o.v[i] = x[i];
+    reinterpret_cast<Pack<float, V>*>(static_cast<float*>(dst) + r * d_latent)[lane] = o;
+  } else {
+    Pack<uint16_t, V> o;
+#pragma unroll
+    for (int i = 0; i < V; ++i) o.v[i] = f32_to_bf16(x[i]);
+    reinterpret_cast<Pack<uint16_t, V>*>(static_cast<uint16_t*>(dst) + r * d_latent)[lane] = o;
   }
+}
+
+template <typename T>
+hipError_t launch_rotate(const T* q, int rows, int d_latent, void* dst, int dst_f32, hipStream_t stream) {
+  const dim3 grid((rows + kMergeWaves - 1) / kMergeWaves);
+  switch (d_latent <= 64 ? 1 : d_latent / 64) {
+    case 1: hipLaunchKernelGGL((rotate_query_kernel<T, 1>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
+    case 2: hipLaunchKernelGGL((rotate_query_kernel<T, 2>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
+    case 4: hipLaunchKernelGGL((rotate_query_kernel<T, 4>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
+    case 8: hipLaunchKernelGGL((rotate_query_kernel<T, 8>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
+    case 16: hipLaunchKernelGGL((rotate_query_kernel<T, 16>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // tile_prefix[b] = sum_{b' < b} ceil(seq_lens[b'] / 32) for b = 0..batch, one block: each thread
@@ -384,15 +374,9 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
 
 hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_latent, void* dst, int dst_f32,
                                hipStream_t stream) {
-  if (d_latent > kMaxLatent) return hipErrorInvalidValue;
-  const dim3 grid((rows + kMergeWaves - 1) / kMergeWaves);
-  if (dtype == 0)
-    hipLaunchKernelGGL(rotate_query_kernel<float>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const float*>(q_lat), rows, d_latent, dst, dst_f32);
-  else
-    hipLaunchKernelGGL(rotate_query_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q_lat), rows, d_latent, dst, dst_f32);
-  return hipGetLastError();
+  if (d_latent > kMaxLatent || (d_latent & (d_latent - 1)) != 0) return hipErrorInvalidValue;
+  if (dtype == 0) return launch_rotate(static_cast<const float*>(q_lat), rows, d_latent, dst, dst_f32, stream);
+  return launch_rotate(static_cast<const uint16_t*>(q_lat), rows, d_latent, dst, dst_f32, stream);
 }
 
 }  // namespace tpla

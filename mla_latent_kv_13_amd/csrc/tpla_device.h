@@ -97,6 +97,73 @@ __device__ __forceinline__ void block_fwht(float* x, int n) {
   __syncthreads();
 }
 
+// V elements of T read or written as one aligned access.
+template <typename T, int V>
+struct alignas(sizeof(T) * V) Pack {
+  T v[V];
+};
+
+// Lane v's value from another lane of its row of 16 (DPP; every lane reads a valid source).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// One butterfly of a Walsh-Hadamard stage across lanes: the pair (lane, lane ^ M) becomes
+// (a + c, a - c), a the value of the lane with bit M clear.  The partner's value comes from a
+// VALU lane swap: DPP within rows of 16 (M = 4: the half-row mirror, then the quad reversal,
+// lands on lane ^ 4), permlane swaps across rows (results: lane with bit M clear, lane with it set).
+template <int M>
+__device__ __forceinline__ float wht_lane_pair(float x, int lane) {
+  if constexpr (M >= 16) {
+    const auto sw = M == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                            : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
+    return (lane & M) ? lo - hi : lo + hi;
+  } else {
+    float other;
+    if constexpr (M == 1) other = dpp_mov<0xb1>(x);                 // quad_perm(1, 0, 3, 2)
+    else if constexpr (M == 2) other = dpp_mov<0x4e>(x);            // quad_perm(2, 3, 0, 1)
+    else if constexpr (M == 4) other = dpp_mov<0x1b>(dpp_mov<0x141>(x));  // row_half_mirror, quad_perm(3, 2, 1, 0)
+    else other = dpp_mov<0x128>(x);                                  // row_ror:8
+    return (lane & M) ? other - x : x + other;
+  }
+}
+
+// In-register orthonormal Walsh-Hadamard transform (Sylvester order) of n values held V per
+// lane: element e = V * lane + r is x[r], n = V * lanes with lanes = n / V a power of two <= 64
+// (lanes past n / V hold values that are never used).  Butterflies on pairs (e, e + span), span
+// increasing: within a lane's registers while span < V, then across lanes; then 1/sqrt(n).
+template <int V>
+__device__ __forceinline__ void wave_wht(float (&x)[V], int n, int lane) {
+#pragma unroll
+  for (int span = 1; span < V; span <<= 1) {
+#pragma unroll
+    for (int r = 0; r < V; ++r) {
+      if ((r & span) == 0) {
+        const float u = x[r], w = x[r + span];
+        x[r] = u + w;
+        x[r + span] = u - w;
+      }
+    }
+  }
+  const int lanes = n / V;
+#define TPLA_WHT_LANE_STAGE(M)                                            \
+  if (lanes > M) {                                                        \
+    _Pragma("unroll") for (int r = 0; r < V; ++r) x[r] = wht_lane_pair<M>(x[r], lane); \
+  }
+  TPLA_WHT_LANE_STAGE(1)
+  TPLA_WHT_LANE_STAGE(2)
+  TPLA_WHT_LANE_STAGE(4)
+  TPLA_WHT_LANE_STAGE(8)
+  TPLA_WHT_LANE_STAGE(16)
+  TPLA_WHT_LANE_STAGE(32)
+#undef TPLA_WHT_LANE_STAGE
+  const float norm = 1.0f / sqrtf(static_cast<float>(n));
+#pragma unroll
+  for (int r = 0; r < V; ++r) x[r] *= norm;
+}
+
 // Row of the cache pool holding token t of sequence b.
 __device__ __forceinline__ int64_t cache_row(const int* __restrict__ block_table, int b, int t, int page_size,
                                              int max_pages_per_seq) {

@@ -44,6 +44,12 @@ SMALL = [
     ("negative_scale", dict(batch=2, heads=64, shards=4, lens=[250, 64], scale=-0.1), {}),
     ("single_tile_and_one_token", dict(batch=3, heads=128, shards=1, lens=[32, 1, 31]), {}),
     ("more_than_64_chunks", dict(batch=2, heads=32, shards=2, lens=[5000, 4100]), dict(chunk_tokens=64)),
+    # Hadamard row widths 256 and 1024 (4 and 16 values per lane) and 32 (fp32, half the lanes idle)
+    ("g2_wht_dl256", dict(batch=2, heads=64, d_latent=256, shards=2, lens=[300, 45], transform="wht"), {}),
+    ("g4_wht_dl1024_paged", dict(batch=2, heads=32, d_latent=1024, shards=4, lens=[200, 70], transform="wht",
+                                 paged=True, page_size=32), {}),
+    ("f32_wht_dl32", dict(batch=2, heads=3, d_latent=32, d_rope=8, shards=2, lens=[40, 7], dtype="f32",
+                          transform="wht"), {}),
 ]
 
 
