@@ -19,7 +19,9 @@ decode (G = 1, batch 32, 128 heads, latent 512 + rope 64, context 4096, bf16);
 the other workloads (TPLA G = 2 / G = 4 at 32K context, paged + Hadamard with
 ragged contexts) are reported in "workloads" unless --headline-only is given; the
 contiguous TPLA workloads also carry "per_device_share": the call of one shard (what one
-of G devices would read and compute) and the G = 1 call over the same cache.
+of G devices would read and compute) and the G = 1 call over the same cache.  "append"
+times latent_cache_append on its own on the paged Hadamard workload's rows: the whole
+cache and one row per sequence, rotated and plain.
 """
 
 from __future__ import annotations
@@ -248,6 +250,60 @@ def time_shard_calls(w: Workload, steps: int, warmup: int, flush: bool):
     return res
 
 
+def time_append(w: Workload, steps: int, warmup: int, flush: bool):
+    """latent_cache_append timed on its own (events around each call) on the rows of a workload:
+    the whole cache at once (as after a prefill) and one row per sequence (one decode step), with
+    the workload's transform and, into a second pool, without rotation.  Re-appending a row at its
+    own slot stores the value it already holds, so the decode inputs stay as they were.
+    Algorithmic bytes: each row read once and written once."""
+    import numpy as np
+    import torch
+
+    c = w.case
+    binding = w.binding
+    dev = "cuda:0"
+    flush_buf = _flush_buffer() if flush else None
+    elem = 2 if c.dtype == "bf16" else 4
+    row_bytes = (c.d_latent + c.d_rope) * elem
+    if c.dtype == "bf16":
+        rows = torch.from_numpy(np.ascontiguousarray(c.rows).view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        rows = torch.from_numpy(np.ascontiguousarray(c.rows, dtype=np.float32)).to(dev)
+    slots = torch.from_numpy(c.slots).to(dev)
+    ends = np.cumsum(c.seq_lens.astype(np.int64))
+    last = torch.from_numpy(ends[c.seq_lens > 0] - 1).to(dev)  # the newest row of each non-empty sequence
+    step_rows, step_slots = rows[last].contiguous(), slots[last].contiguous()
+    plain = binding.Desc(c.dtype, c.d_latent, c.d_rope, c.page_size, c.num_pages, c.max_pages_per_seq, "identity")
+    scratch = torch.empty_like(w.pool)
+
+    def timed(desc, pool, r, sl, n_steps):
+        for _ in range(warmup):
+            binding.latent_cache_append(desc, pool, r, sl)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_steps)]
+        for e in ev:
+            if flush_buf is not None:
+                flush_buf.sum()
+            e[0].record()
+            binding.latent_cache_append(desc, pool, r, sl)
+            e[1].record()
+        torch.cuda.synchronize()
+        ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
+        n = int(r.shape[0])
+        gbs = 2 * n * row_bytes / (ms * 1e-3) / 1e9
+        return {"rows": n, "ms_mean": ms, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+    res = {"workload": c.name, "row_bytes": row_bytes}
+    for name, desc, pool in ((c.transform, w.desc, w.pool), ("identity_into_second_pool", plain, scratch)):
+        if name == "identity_into_second_pool" and c.transform == "identity":
+            continue
+        res[name] = {"whole_cache": timed(desc, pool, rows, slots, max(3, steps // 3)),
+                     "one_row_per_sequence": timed(desc, pool, step_rows, step_slots, steps)}
+    del rows, slots, step_rows, step_slots, scratch
+    torch.cuda.empty_cache()
+    return res
+
+
 def streaming_bandwidth(steps: int = 10):
     """What plain streaming reaches on this card with the runtime's own kernels: a
     device-to-device copy of 1 GiB (1 GiB read plus 1 GiB written), and a full reduction of a
@@ -398,6 +454,8 @@ def main():
             if w.case.shards > 1 and not w.case.paged:
                 others[w.case.name]["per_device_share"] = time_shard_calls(w, args.extra_steps, args.warmup,
                                                                            not args.no_flush)
+            if w.case.transform != "identity":
+                line["append"] = time_append(w, args.extra_steps, args.warmup, not args.no_flush)
             log(f"workload {cfg}: {json.dumps(others[w.case.name])}")
             del w
             torch.cuda.empty_cache()
