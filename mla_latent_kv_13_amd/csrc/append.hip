@@ -13,38 +13,57 @@ constexpr int kMaxLatent = 1024;
 
 constexpr int kRowsPerBlock = kThreads / 64;  // one wave per appended row
 
-// One wave per row: lane l holds latent elements V*l .. V*l+V-1 (V = d_latent / 64, or 1 with
-// lanes >= d_latent idle), rotated in registers.
+// One wave per row at a time, the grid striding over the rows: lane l holds latent elements
+// V*l .. V*l+V-1 (V = d_latent / 64, or 1 with lanes >= d_latent idle), rotated in registers,
+// and rope-key piece l (16 bytes; the first 64 pieces), copied unchanged.  The next row's loads
+// are issued before this row is rotated (a wave's last prefetch re-reads row n - 1, unused).
 template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void append_wht_kernel(T* __restrict__ cache, const T* __restrict__ rows,
                                                                const int64_t* __restrict__ slots, int64_t n,
                                                                int d_latent, int d_rope) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kRowsPerBlock;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
   if (i >= n) return;
   const int64_t D = d_latent + d_rope;
-  const T* src = rows + i * D;
-  T* dst = cache + slots[i] * D;
   const int lanes = d_latent / V;  // lanes holding latent elements (<= 64)
   const bool on = lane < lanes;
-  Pack<T, V> p = on ? reinterpret_cast<const Pack<T, V>*>(src)[lane] : Pack<T, V>{};
-  float x[V];
+  const int pieces = d_rope * static_cast<int>(sizeof(T)) / 16;  // rope key in 16-byte pieces
+  const bool rope_on = lane < pieces;
+  // every lane loads in bounds: idle lanes repeat piece 0 (of the latent when there is no rope)
+  auto load = [&](int64_t r, Pack<T, V>& p, uint4& rk) {
+    const T* src = rows + r * D;
+    p = reinterpret_cast<const Pack<T, V>*>(src)[on ? lane : 0];
+    rk = reinterpret_cast<const uint4*>(pieces > 0 ? src + d_latent : src)[rope_on ? lane : 0];
+  };
+  Pack<T, V> p;
+  uint4 rk;
+  load(i, p, rk);
+  for (; i < n; i += stride) {
+    Pack<T, V> pn;
+    uint4 rkn;
+    load(min(i + stride, n - 1), pn, rkn);
+    T* dst = cache + slots[i] * D;
+    float x[V];
 #pragma unroll
-  for (int r = 0; r < V; ++r) x[r] = load_as_f32(&p.v[r]);
-  wave_wht(x, d_latent, lane);
+    for (int r = 0; r < V; ++r) x[r] = on ? load_as_f32(&p.v[r]) : 0.f;
+    wave_wht(x, d_latent, lane);
 #pragma unroll
-  for (int r = 0; r < V; ++r) p.v[r] = store_from_f32<T>(x[r]);
-  if (on) reinterpret_cast<Pack<T, V>*>(dst)[lane] = p;
-  // rope key: unchanged, 16 bytes per lane (d_latent and d_rope elements are multiples of 16 bytes)
-  const int pieces = d_rope * static_cast<int>(sizeof(T)) / 16;
-  for (int k = lane; k < pieces; k += 64)
-    reinterpret_cast<uint4*>(dst + d_latent)[k] = reinterpret_cast<const uint4*>(src + d_latent)[k];
+    for (int r = 0; r < V; ++r) p.v[r] = store_from_f32<T>(x[r]);
+    if (on) reinterpret_cast<Pack<T, V>*>(dst)[lane] = p;
+    if (rope_on) reinterpret_cast<uint4*>(dst + d_latent)[lane] = rk;
+    for (int k = lane + 64; k < pieces; k += 64)  // rope keys wider than 64 pieces
+      reinterpret_cast<uint4*>(dst + d_latent)[k] = reinterpret_cast<const uint4*>(rows + i * D + d_latent)[k];
+    p = pn;
+    rk = rkn;
+  }
 }
 
 template <typename T>
 hipError_t launch_wht(T* cache, const T* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
                       hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((n + kRowsPerBlock - 1) / kRowsPerBlock));
+  // enough waves to keep every CU busy, each then striding over the rows
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>((n + kRowsPerBlock - 1) / kRowsPerBlock, 256 * 16)));
   switch (d_latent <= 64 ? 1 : d_latent / 64) {
     case 1: hipLaunchKernelGGL((append_wht_kernel<T, 1>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
     case 2: hipLaunchKernelGGL((append_wht_kernel<T, 2>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;

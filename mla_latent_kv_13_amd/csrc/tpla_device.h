@@ -119,20 +119,20 @@ __device__ __forceinline__ float wht_lane_pair(float x, int lane) {
     const auto sw = M == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
                             : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     const float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
-    return (lane & M) ? lo - hi : lo + hi;
+    return __builtin_fmaf(hi, (lane & M) ? -1.0f : 1.0f, lo);  // lo -/+ hi, one rounding
   } else {
     float other;
     if constexpr (M == 1) other = dpp_mov<0xb1>(x);                 // quad_perm(1, 0, 3, 2)
     else if constexpr (M == 2) other = dpp_mov<0x4e>(x);            // quad_perm(2, 3, 0, 1)
     else if constexpr (M == 4) other = dpp_mov<0x1b>(dpp_mov<0x141>(x));  // row_half_mirror, quad_perm(3, 2, 1, 0)
     else other = dpp_mov<0x128>(x);                                  // row_ror:8
-    return (lane & M) ? other - x : x + other;
+    return __builtin_fmaf(x, (lane & M) ? -1.0f : 1.0f, other);  // other -/+ x, one rounding
   }
 }
 
 // In-register orthonormal Walsh-Hadamard transform (Sylvester order) of n values held V per
-// lane: element e = V * lane + r is x[r], n = V * lanes with lanes = n / V a power of two <= 64
-// (lanes past n / V hold values that are never used).  Butterflies on pairs (e, e + span), span
+// lane: element e = V * lane + r is x[r], n = V * lanes with lanes = n / V a power of two: 64
+// when V > 1, up to 64 when V = 1 (lanes past n hold values that are never used).  Butterflies on pairs (e, e + span), span
 // increasing: within a lane's registers while span < V, then across lanes; then 1/sqrt(n).
 template <int V>
 __device__ __forceinline__ void wave_wht(float (&x)[V], int n, int lane) {
@@ -149,7 +149,7 @@ __device__ __forceinline__ void wave_wht(float (&x)[V], int n, int lane) {
   }
   const int lanes = n / V;
 #define TPLA_WHT_LANE_STAGE(M)                                            \
-  if (lanes > M) {                                                        \
+  if (V > 1 || lanes > M) {                                               \
     _Pragma("unroll") for (int r = 0; r < V; ++r) x[r] = wht_lane_pair<M>(x[r], lane); \
   }
   TPLA_WHT_LANE_STAGE(1)
