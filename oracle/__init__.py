@@ -16,4 +16,5 @@ from .tpla_oracle import (  # noqa: F401
     tpla_decode_sharded,
     mla_decode_absorbed,
     mla_unabsorbed_bruteforce,
+    value_up_projection,
 )

@@ -67,6 +67,7 @@ __all__ = [
     "tpla_decode_sharded",
     "mla_decode_absorbed",
     "mla_unabsorbed_bruteforce",
+    "value_up_projection",
 ]
 
 
@@ -226,6 +227,31 @@ def mla_decode_absorbed(pool, block_table, seq_lens, q_lat, q_rope, scale: float
     out, lse = tpla_decode_sharded(pool, block_table, seq_lens, q_lat, q_rope, scale,
                                    num_shards=1, transform=transform)
     return out, lse[:, 0, :]
+
+
+def value_up_projection(out_latent, w_uv) -> np.ndarray:
+    """The value up-projection that follows latent-space attention: for each
+    sequence b and head h, ``out_v[b, h] = w_uv[h] @ out_latent[b, h]``.
+
+    Shapes: out_latent [B, H, d_c] (a decode result in the caller's latent
+    frame), w_uv [H, d_v, d_c] (each head's value rows of kv_b_proj, mapping
+    the latent to that head's value), result [B, H, d_v].  With the key
+    up-projection absorbed into the query, attention runs in latent space and
+    W_UV is applied afterwards ([REV] referee report, significance: matrix
+    absorption; [FR] Background: kv_b_proj sharded per head, o_proj rowwise,
+    then the all-reduce).  Applied to one device's shard subset (reading A13)
+    this gives that device's operand of the all-reduce; the operands of all
+    shards add up to the projection of the full output (linearity, reading A1).
+    """
+    out_latent = np.asarray(out_latent, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    batch, heads, d_c = out_latent.shape
+    if w_uv.shape[0] != heads or w_uv.shape[2] != d_c:
+        raise ValueError("w_uv must be [heads, d_v, d_latent]")
+    out = np.empty((batch, heads, w_uv.shape[1]), dtype=np.float64)
+    for h in range(heads):
+        out[:, h, :] = out_latent[:, h, :] @ w_uv[h].T  # rows times W_UV[h]^T = W_UV[h] applied to each row
+    return out
 
 
 def mla_unabsorbed_bruteforce(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale: float) -> np.ndarray:

@@ -79,10 +79,12 @@ def pin_p1_absorbed_equals_unabsorbed(orc):
     q_lat = np.stack([np.stack([w_uk[h].T @ q_nope[b, h] for h in range(H)]) for b in range(B)])
     out, lse = orc.mla_decode_absorbed(pool, None, seq_lens, q_lat, q_rope, scale)
     assert out.shape == (B, H, d_c) and lse.shape == (B, H)
+    # then the value up-projection the absorbed form applies afterwards
+    projected = orc.value_up_projection(out, w_uv)
+    assert projected.shape == (B, H, d_v)
     for b in range(B):
         ref = orc.mla_unabsorbed_bruteforce(lat[b], rope[b], q_nope[b], q_rope[b], w_uk, w_uv, scale)
-        got = np.stack([w_uv[h] @ out[b, h] for h in range(H)])
-        assert _rel(got, ref) <= 1e-12, ("P1", b, _rel(got, ref))
+        assert _rel(projected[b], ref) <= 1e-12, ("P1", b, _rel(projected[b], ref))
 
 
 def pin_p1b_bruteforce_closed_form(orc):
@@ -99,6 +101,46 @@ def pin_p1b_bruteforce_closed_form(orc):
     got = orc.mla_unabsorbed_bruteforce(c, np.zeros((2, d_r)), np.ones((H, d_nope)),
                                         np.zeros((H, d_r)), w_uk, w_uv, 1.0)
     assert np.allclose(got, [[0.75 * math.log(3.0), 0.0]], rtol=1e-14, atol=1e-15), got
+
+
+# ---------------------------------------------------------------- P9
+def pin_p9_value_projection(orc):
+    """The value up-projection on its own: W_UV[h] = I returns the latent
+    output unchanged; a one-hot W_UV[h] (row v reads latent column c) moves
+    out_latent[b, h, c] to out_v[b, h, v] for that head only, so a transposed
+    or head-shifted weight fails; and the projections of the shard subsets of
+    a G = 2 call, with and without the rotation, add up to the projection of
+    the full call ([FR] Background: o_proj rowwise then all-reduce; reading A1)."""
+    rng = np.random.default_rng(91)
+    B, H, d_c, d_v = 2, 3, 8, 5
+    y = rng.standard_normal((B, H, d_c))
+    eye = np.broadcast_to(np.eye(d_c), (H, d_c, d_c))
+    assert np.array_equal(orc.value_up_projection(y, eye), y)
+    w = np.zeros((H, d_v, d_c))
+    picks = {0: (1, 6), 1: (4, 0), 2: (0, 3)}  # head -> (v, c)
+    for h, (v, c) in picks.items():
+        w[h, v, c] = 2.0
+    got = orc.value_up_projection(y, w)
+    want = np.zeros((B, H, d_v))
+    for h, (v, c) in picks.items():
+        want[:, h, v] = 2.0 * y[:, h, c]
+    assert np.array_equal(got, want), ("P9 one-hot", got, want)
+    pool, seq_lens, q_lat, q_rope = _random_problem(92, B=2, H=3, d_c=16, d_r=4, lens=(6, 11))
+    w_uv = rng.standard_normal((3, 7, 16))
+    for transform in ("identity", "wht"):
+        if transform == "wht":
+            flat = pool.reshape(-1, pool.shape[-1])
+            used = ~np.isnan(flat[:, 0])
+            store = np.full_like(flat, np.nan)
+            store = orc.latent_cache_append(store[None], flat[used], np.flatnonzero(used), 16, "wht", "f64")[0]
+            src = store.reshape(pool.shape)
+        else:
+            src = pool
+        full, _ = orc.tpla_decode_sharded(src, None, seq_lens, q_lat, q_rope, 0.3, 2, transform=transform)
+        parts = [orc.tpla_decode_sharded(src, None, seq_lens, q_lat, q_rope, 0.3, 2, s, 1, transform=transform)[0]
+                 for s in range(2)]
+        summed = orc.value_up_projection(parts[0], w_uv) + orc.value_up_projection(parts[1], w_uv)
+        assert _rel(summed, orc.value_up_projection(full, w_uv)) <= 1e-13, ("P9 shard sum", transform)
 
 
 # ---------------------------------------------------------------- P2
@@ -442,6 +484,7 @@ ALL_PINS = [
     pin_p6b_empty_sequence,
     pin_p7_not_exact_for_g2,
     pin_p8_softmax_lse_scipy,
+    pin_p9_value_projection,
     pin_paged_gather,
     pin_append,
     pin_bf16_rne,

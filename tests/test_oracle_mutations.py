@@ -35,6 +35,8 @@ MUTATIONS = {
     "append_no_rounding": ("flat[slot, :d_latent] = _store(lat, dtype)", "flat[slot, :d_latent] = lat"),
     "shard_output_summed_not_placed": ("y[:, cols] = (p @ c_lat[:, cols]) / z", "y[:, :w] += (p @ c_lat[:, cols]) / z"),
     "rope_from_latent": ("k_rope = rows[:, d_c:]", "k_rope = rows[:, :d_c][:, :rows.shape[1] - d_c]"),
+    "projection_transposed_weight": ("out_latent[:, h, :] @ w_uv[h].T", "out_latent[:, h, :] @ w_uv[h][:, ::-1].T"),
+    "projection_wrong_head": ("out_latent[:, h, :] @ w_uv[h].T", "out_latent[:, h, :] @ w_uv[(h + 1) % heads].T"),
     "empty_lse_zero": ("lse = np.full((batch, shard_count, heads), -np.inf, dtype=np.float64)",
                        "lse = np.full((batch, shard_count, heads), 0.0, dtype=np.float64)"),
 }
