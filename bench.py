@@ -21,7 +21,8 @@ ragged contexts) are reported in "workloads" unless --headline-only is given; th
 contiguous TPLA workloads also carry "per_device_share": the call of one shard (what one
 of G devices would read and compute) and the G = 1 call over the same cache.  "append"
 times latent_cache_append on its own on the paged Hadamard workload's rows: the whole
-cache and one row per sequence, rotated and plain.
+cache and one row per sequence, rotated and plain; "value_up_projection" times the value
+up-projection that follows the decode (DeepSeek-V3 shapes, bf16 weights).
 """
 
 from __future__ import annotations
@@ -304,6 +305,39 @@ def time_append(w: Workload, steps: int, warmup: int, flush: bool):
     return res
 
 
+def time_value_projection(steps: int, warmup: int, flush: bool, batch=32, heads=128, d_latent=512, d_v=128):
+    """tpla_value_up_projection timed on its own (events around each call) at DeepSeek-V3 shapes
+    (value width 128 per head) with seeded bf16 weights, against its algorithmic bytes: the
+    weights once, the latent-frame output read once and the projected output written once."""
+    import torch
+
+    from mla_latent_kv_13_amd import binding, inputs
+
+    o, w = inputs.make_value_projection(2, batch=batch, heads=heads, d_latent=d_latent, d_v=d_v)
+    o_t = torch.from_numpy(o).to("cuda:0")
+    w_t = torch.from_numpy(w.view("int16")).view(torch.bfloat16).to("cuda:0")
+    out = torch.empty((batch, heads, d_v), dtype=torch.float32, device="cuda:0")
+    flush_buf = _flush_buffer() if flush else None
+    for _ in range(warmup):
+        binding.tpla_value_up_projection(o_t, w_t, out_v=out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        if flush_buf is not None:
+            flush_buf.sum()
+        e[0].record()
+        binding.tpla_value_up_projection(o_t, w_t, out_v=out)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
+    nbytes = heads * d_v * d_latent * 2 + batch * heads * d_latent * 4 + batch * heads * d_v * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del o_t, w_t, out
+    return {"shape": {"batch": batch, "heads": heads, "d_latent": d_latent, "d_v": d_v, "weights": "bf16"},
+            "ms_mean": ms, "algorithmic_bytes": nbytes, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
+            "bound": "hbm"}
+
+
 def streaming_bandwidth(steps: int = 10):
     """What plain streaming reaches on this card with the runtime's own kernels: a
     device-to-device copy of 1 GiB (1 GiB read plus 1 GiB written), and a full reduction of a
@@ -461,6 +495,7 @@ def main():
             torch.cuda.empty_cache()
         line["workloads"] = others
     if not args.headline_only:
+        line["value_up_projection"] = time_value_projection(args.extra_steps, args.warmup, not args.no_flush)
         line["achievable_streaming"] = streaming_bandwidth()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_case)

@@ -196,6 +196,29 @@ int32_t mla_decode_absorbed(const tpla_cache_desc_t* desc, const void* cache,
                             float* out, float* lse, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Value up-projection of a decode result: with the key up-projection absorbed
+ * into the query, attention runs in latent space and each head's value rows of
+ * kv_b_proj are applied after it ([REV] referee report, significance: matrix
+ * absorption; [FR] Background / problem: kv_b_proj sharded per head, o_proj
+ * rowwise, then the all-reduce):
+ *   out_v[b,h,:] = W_UV[h] . o[b,h,:]     for b < batch, h < heads
+ *   o      device, fp32 [batch, heads, d_latent]: the `out` of
+ *          tpla_decode_sharded / mla_decode_absorbed (the caller's latent frame).
+ *          For one device's shard subset the result is that device's operand of
+ *          the all-reduce; the fp32 sum of the operands of all shards is the
+ *          projection of the full output.
+ *   w_uv   device, [heads, d_v, d_latent] in w_dtype (TPLA_F32 or TPLA_BF16):
+ *          row v of head h maps the latent to value component v.
+ *   out_v  device, fp32 [batch, heads, d_v], fully overwritten.
+ * With bf16 weights and d_latent a multiple of 16 the product runs on the matrix
+ * cores: o enters as a bf16 value plus its bf16 remainder (two products into one
+ * fp32 sum), so about 16 significant bits of o take part; otherwise fp32
+ * arithmetic.  batch or heads 0 is a no-op; heads <= 65535.  Alignment: o, w_uv,
+ * out_v 16 bytes.  No workspace. */
+int32_t tpla_value_up_projection(int32_t w_dtype, const float* o, const void* w_uv,
+                                 int32_t batch, int32_t heads, int32_t d_latent, int32_t d_v,
+                                 float* out_v, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

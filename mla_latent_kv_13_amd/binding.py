@@ -26,7 +26,8 @@ KERNELS = {"auto": 0, "generic": 1, "mfma": 2}
 SCHEDULES = {"auto": 0, "chunked": 1, "balanced": 2}
 
 EXPORTED = ["tpla_abi_version", "tpla_status_string", "tpla_last_error", "tpla_workspace_size",
-            "latent_cache_append", "tpla_decode_sharded", "tpla_decode_sharded_ex", "mla_decode_absorbed"]
+            "latent_cache_append", "tpla_decode_sharded", "tpla_decode_sharded_ex", "mla_decode_absorbed",
+            "tpla_value_up_projection"]
 
 
 class TplaError(RuntimeError):
@@ -95,6 +96,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mla_decode_absorbed.restype = _I32
     lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.tpla_value_up_projection.restype = _I32
+    lib.tpla_value_up_projection.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P]
     _LIB = lib
     return lib
 
@@ -219,3 +222,21 @@ def mla_decode_absorbed(desc: Desc, cache: torch.Tensor, block_table: torch.Tens
                                    max_seq_len, _ptr(q_latent), _ptr(q_rope), ctypes.c_float(scale), _ptr(out),
                                    _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def tpla_value_up_projection(o: torch.Tensor, w_uv: torch.Tensor, out_v: torch.Tensor | None = None, stream=None):
+    """out_v[b, h] = w_uv[h] @ o[b, h]; o fp32 [B, H, d_latent], w_uv [H, d_v, d_latent] (fp32 or bf16).
+    Returns out_v fp32 [B, H, d_v]."""
+    if o.dtype != torch.float32 or w_uv.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("o must be fp32 and w_uv fp32 or bf16")
+    batch, heads, d_latent = (int(x) for x in o.shape)
+    if tuple(w_uv.shape[::2]) != (heads, d_latent):
+        raise ValueError("w_uv must be [heads, d_v, d_latent]")
+    d_v = int(w_uv.shape[1])
+    if out_v is None:
+        out_v = torch.empty((batch, heads, d_v), dtype=torch.float32, device=o.device)
+    w_dtype = DTYPES["bf16"] if w_uv.dtype == torch.bfloat16 else DTYPES["f32"]
+    lib = load_library()
+    _check(lib.tpla_value_up_projection(w_dtype, _ptr(o), _ptr(w_uv), batch, heads, d_latent, d_v, _ptr(out_v),
+                                        _stream(stream)))
+    return out_v

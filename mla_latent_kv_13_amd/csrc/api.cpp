@@ -331,6 +331,22 @@ int32_t latent_cache_append(const tpla_cache_desc_t* desc, void* cache, const vo
   return ok();
 }
 
+int32_t tpla_value_up_projection(int32_t w_dtype, const float* o, const void* w_uv, int32_t batch, int32_t heads,
+                                 int32_t d_latent, int32_t d_v, float* out_v, void* stream) {
+  if (w_dtype != TPLA_F32 && w_dtype != TPLA_BF16) return fail(TPLA_ERR_UNSUPPORTED, "w_dtype %d is not fp32 or bf16", w_dtype);
+  if (batch < 0 || heads < 0 || d_latent < 1 || d_v < 1)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 0, d_latent and d_v >= 1");
+  if (batch == 0 || heads == 0) return ok();
+  if (!o || !w_uv || !out_v) return fail(TPLA_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  if (!aligned(o, 16) || !aligned(w_uv, 16) || !aligned(out_v, 16))
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "o, w_uv and out_v must be 16-byte aligned");
+  if (heads > 65535 || batch > 65535 * 32) return fail(TPLA_ERR_UNSUPPORTED, "heads <= 65535 and batch <= 2097120");
+  const hipError_t e = tpla::launch_up_project(o, w_uv, w_dtype, batch, heads, d_latent, d_v, out_v,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "up-projection launch");
+  return ok();
+}
+
 int32_t tpla_decode_sharded(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
                             const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len,
                             const void* q_latent, const void* q_rope, float scale, int32_t num_shards,

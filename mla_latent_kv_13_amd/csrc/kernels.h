@@ -69,5 +69,8 @@ hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_lat
                                hipStream_t stream);
 hipError_t launch_append(void* cache, const void* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
                          int dtype, int wht, hipStream_t stream);
+// out_v[b,h,:] = W_UV[h] . o[b,h,:]; w_dtype 0 = fp32, 1 = bf16 weights [heads, d_v, d_latent].
+hipError_t launch_up_project(const float* o, const void* w_uv, int w_dtype, int batch, int heads, int d_latent,
+                             int d_v, float* out_v, hipStream_t stream);
 
 }  // namespace tpla

@@ -15,6 +15,11 @@ Recipe (one generator per tensor, ``np.random.default_rng([case_seed, tensor_id]
   tensor 5  context lengths, integers uniform in [lo, hi] inclusive
   tensor 6  page permutation for the paged layout
 
+Value up-projection inputs (``make_value_projection``, its own seed): tensor 0 the latent-frame
+attention output o [B, H, d_c] (float32 normals), tensor 1 the per-head value weights
+W_UV [H, d_v, d_c], normals scaled by 1/sqrt(d_c) (the spread of a trained projection's
+rows), in the weight dtype.
+
 Normals are drawn as float32.  bf16 cases round them to bfloat16 with
 round-to-nearest-even and keep the raw 16-bit patterns (uint16).  Rows of a
 page beyond a sequence's length, and pool pages no sequence uses, are filled
@@ -215,3 +220,11 @@ def make_config(cfg: int, *, place_rows: bool | None = None) -> Case:
     if place_rows is None:
         place_rows = kw.get("transform", "identity") == "identity"
     return make_case(cfg, place_rows=place_rows, **kw)
+
+
+def make_value_projection(seed: int, *, batch: int, heads: int, d_latent: int, d_v: int, dtype: str = "bf16"):
+    """Seeded (o [B, H, d_c] float32, W_UV [H, d_v, d_c] in ``dtype``) for the value up-projection."""
+    o = np.random.default_rng([seed, 0]).standard_normal((batch, heads, d_latent), dtype=np.float32)
+    w = np.random.default_rng([seed, 1]).standard_normal((heads, d_v, d_latent), dtype=np.float32)
+    w = (w * np.float32(1.0 / math.sqrt(d_latent))).astype(np.float32)
+    return o, _to_dtype(w, dtype)

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("latent_cache_append", "tpla_decode_sharded", "mla_decode_absorbed", "tpla_workspace_size"):
+    for required in ("latent_cache_append", "tpla_decode_sharded", "mla_decode_absorbed", "tpla_workspace_size",
+                     "tpla_value_up_projection"):
         assert required in names
     assert set(names) == set(binding.EXPORTED)
 
@@ -135,3 +136,35 @@ def test_bad_descriptor(lib):
     odd = binding.Desc("bf16", 512, 60, 64, 10, 16, "identity")  # 60 is not a multiple of 8
     st, msg = _decode_raw(lib, odd)
     assert st == 2
+
+
+def _up_raw(lib, **kw):
+    """tpla_value_up_projection with fake (never dereferenced) device addresses; only for
+    arguments that validation settles before anything is enqueued."""
+    a = dict(w_dtype=1, o=0x10000, w=0x20000, batch=4, heads=8, d_latent=512, d_v=128, out=0x30000)
+    a.update(kw)
+    p = ctypes.c_void_p
+    st = lib.tpla_value_up_projection(a["w_dtype"], p(a["o"] or None), p(a["w"] or None), a["batch"], a["heads"],
+                                      a["d_latent"], a["d_v"], p(a["out"] or None), None)
+    return st, lib.tpla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w_dtype=7), 2),
+    (dict(batch=-1), 1),
+    (dict(d_v=0), 1),
+    (dict(d_latent=0), 1),
+    (dict(o=0), 1),
+    (dict(w=0x20008), 1),          # misaligned weights
+    (dict(heads=70000), 2),
+])
+def test_up_projection_validation_before_launch(lib, kw, status):
+    st, msg = _up_raw(lib, **kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_up_projection_empty_is_a_no_op(lib):
+    # nothing is enqueued, so no device is touched: fine without a GPU
+    assert _up_raw(lib, batch=0, o=0, w=0, out=0)[0] == 0
+    assert _up_raw(lib, heads=0, o=0, w=0, out=0)[0] == 0
