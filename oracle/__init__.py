@@ -17,4 +17,5 @@ from .tpla_oracle import (  # noqa: F401
     mla_decode_absorbed,
     mla_unabsorbed_bruteforce,
     value_up_projection,
+    merge_context_parts,
 )

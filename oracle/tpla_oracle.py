@@ -68,6 +68,7 @@ __all__ = [
     "mla_decode_absorbed",
     "mla_unabsorbed_bruteforce",
     "value_up_projection",
+    "merge_context_parts",
 ]
 
 
@@ -252,6 +253,54 @@ def value_up_projection(out_latent, w_uv) -> np.ndarray:
     for h in range(heads):
         out[:, h, :] = out_latent[:, h, :] @ w_uv[h].T  # rows times W_UV[h]^T = W_UV[h] applied to each row
     return out
+
+
+def merge_context_parts(out_parts, lse_parts, num_shards: int, shard_begin: int = 0,
+                        shard_count: int | None = None, transform: str = "identity"):
+    """Decode result over a whole context from the results over disjoint parts of it.
+
+    The exact alternative that splits the context instead of the latent: each
+    part (one device's tokens of every sequence) is decoded on its own, then
+    the parts are combined by log-sum-exp ([FR] Directions under investigation:
+    context parallelism, a sequence split with a log-sum-exp merge).  Inputs are
+    P results of ``tpla_decode_sharded`` with the same shards and transform:
+    out_parts [P, B, H, d_c], lse_parts [P, B, n, H].  For each computed shard
+    s (local index i), with y_p = H out_p under the Hadamard transform (H is its
+    own inverse), else y_p = out_p, and o_p,s = y_p's columns of shard s:
+
+      lse_i = log sum_p exp(lse_p,i),   o_s = sum_p exp(lse_p,i - lse_i) o_p,s
+
+    and out = H y (or y) with y holding o_s in its shard's columns, zeros
+    elsewhere.  Parts with lse = -inf (no tokens) contribute nothing; a shard
+    with no tokens in any part gives o_s = 0 and lse = -inf (reading A10).
+    """
+    out_parts = np.asarray(out_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    parts, batch, heads, d_c = out_parts.shape
+    if d_c % num_shards != 0:
+        raise ValueError("the latent width must split evenly into the shards")
+    w = d_c // num_shards
+    if shard_count is None:
+        shard_count = num_shards - shard_begin
+    hmat = hadamard(d_c) if transform == "wht" else None
+    out = np.zeros((batch, heads, d_c), dtype=np.float64)
+    lse = np.full((batch, shard_count, heads), -np.inf, dtype=np.float64)
+    for b in range(batch):
+        for h in range(heads):
+            ys = [out_parts[p, b, h] @ hmat if hmat is not None else out_parts[p, b, h] for p in range(parts)]
+            y = np.zeros(d_c, dtype=np.float64)
+            for i, s in enumerate(range(shard_begin, shard_begin + shard_count)):
+                l = lse_parts[:, b, i, h]
+                if np.all(np.isneginf(l)):
+                    continue
+                m = l.max()
+                z = np.exp(l - m).sum()
+                lse[b, i, h] = m + np.log(z)
+                cols = slice(s * w, (s + 1) * w)
+                for p in range(parts):
+                    y[cols] += np.exp(l[p] - lse[b, i, h]) * ys[p][cols]
+            out[b, h] = y @ hmat if hmat is not None else y
+    return out, lse
 
 
 def mla_unabsorbed_bruteforce(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale: float) -> np.ndarray:

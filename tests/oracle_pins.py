@@ -143,6 +143,52 @@ def pin_p9_value_projection(orc):
         assert _rel(summed, orc.value_up_projection(full, w_uv)) <= 1e-13, ("P9 shard sum", transform)
 
 
+# ---------------------------------------------------------------- P10
+def pin_p10_context_split_merge(orc):
+    """Decoding each part of a split context and merging the parts by
+    log-sum-exp gives the decode of the whole context ([FR] Directions: exact
+    context parallelism, sequence split + log-sum-exp merge).  The whole-context
+    decode is computed independently by the oracle's own decode, so a wrong
+    weight, a missing un-rotation or a shard mix-up fails.  Covers G = 1, G = 2
+    with a shard subset, the Hadamard transform, a part with no tokens and a
+    sequence with none at all."""
+    rng = np.random.default_rng(101)
+    B, H, d_c, d_r = 3, 2, 16, 4
+    lens = (13, 5, 0)
+    lat = [rng.standard_normal((t, d_c)) * 2.0 for t in lens]
+    rope = [rng.standard_normal((t, d_r)) for t in lens]
+    q_lat = rng.standard_normal((B, H, d_c))
+    q_rope = rng.standard_normal((B, H, d_r))
+    cuts = [(0, 4), (4, 4), (4, 13)]  # token ranges of the parts; the second is empty for every sequence
+    for transform, G, s0, n in (("identity", 1, 0, 1), ("identity", 2, 1, 1), ("wht", 2, 0, 2), ("wht", 4, 1, 2)):
+        def pool_of(ranges):
+            parts_lat = [lat[b][min(a, lens[b]):min(e, lens[b])] for b, (a, e) in enumerate(ranges)]
+            parts_rope = [rope[b][min(a, lens[b]):min(e, lens[b])] for b, (a, e) in enumerate(ranges)]
+            pool, seq_lens = _pool(parts_lat, parts_rope, max_len=13)
+            if transform == "wht":
+                flat = pool.reshape(-1, pool.shape[-1])
+                used = ~np.isnan(flat[:, 0])
+                if np.any(used):
+                    store = orc.latent_cache_append(np.full_like(flat, np.nan)[None], flat[used],
+                                                    np.flatnonzero(used), d_c, "wht", "f64")[0]
+                    pool = store.reshape(pool.shape)
+            return pool, seq_lens
+        full_pool, full_lens = pool_of([(0, 13)] * B)
+        want, want_lse = orc.tpla_decode_sharded(full_pool, None, full_lens, q_lat, q_rope, 0.4, G, s0, n,
+                                                 transform=transform)
+        outs, lses = [], []
+        for a, e in cuts:
+            pool, seq_lens = pool_of([(a, e)] * B)
+            o, l = orc.tpla_decode_sharded(pool, None, seq_lens, q_lat, q_rope, 0.4, G, s0, n, transform=transform)
+            outs.append(o)
+            lses.append(l)
+        got, got_lse = orc.merge_context_parts(np.stack(outs), np.stack(lses), G, s0, n, transform=transform)
+        assert np.max(np.abs(got - want)) <= 1e-12, ("P10 out", transform, G, np.max(np.abs(got - want)))
+        assert np.array_equal(np.isneginf(got_lse), np.isneginf(want_lse)), ("P10 lse -inf", transform, G)
+        fin = ~np.isneginf(want_lse)
+        assert np.max(np.abs(got_lse[fin] - want_lse[fin])) <= 1e-12, ("P10 lse", transform, G)
+
+
 # ---------------------------------------------------------------- P2
 def pin_p2_hadamard_invariance_g1(orc):
     """At G = 1 an orthogonal rotation of both query and latent leaves the
@@ -485,6 +531,7 @@ ALL_PINS = [
     pin_p7_not_exact_for_g2,
     pin_p8_softmax_lse_scipy,
     pin_p9_value_projection,
+    pin_p10_context_split_merge,
     pin_paged_gather,
     pin_append,
     pin_bf16_rne,

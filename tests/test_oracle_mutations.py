@@ -37,6 +37,10 @@ MUTATIONS = {
     "rope_from_latent": ("k_rope = rows[:, d_c:]", "k_rope = rows[:, :d_c][:, :rows.shape[1] - d_c]"),
     "projection_transposed_weight": ("out_latent[:, h, :] @ w_uv[h].T", "out_latent[:, h, :] @ w_uv[h][:, ::-1].T"),
     "projection_wrong_head": ("out_latent[:, h, :] @ w_uv[h].T", "out_latent[:, h, :] @ w_uv[(h + 1) % heads].T"),
+    "merge_weight_without_lse": ("y[cols] += np.exp(l[p] - lse[b, i, h]) * ys[p][cols]", "y[cols] += ys[p][cols] / parts"),
+    "merge_no_unrotation": ("ys = [out_parts[p, b, h] @ hmat if hmat is not None else out_parts[p, b, h] for p in range(parts)]",
+                            "ys = [out_parts[p, b, h] for p in range(parts)]"),
+    "merge_lse_without_max": ("lse[b, i, h] = m + np.log(z)", "lse[b, i, h] = np.log(z)"),
     "empty_lse_zero": ("lse = np.full((batch, shard_count, heads), -np.inf, dtype=np.float64)",
                        "lse = np.full((batch, shard_count, heads), 0.0, dtype=np.float64)"),
 }
