@@ -22,7 +22,8 @@ contiguous TPLA workloads also carry "per_device_share": the call of one shard (
 of G devices would read and compute) and the G = 1 call over the same cache.  "append"
 times latent_cache_append on its own on the paged Hadamard workload's rows: the whole
 cache and one row per sequence, rotated and plain; "value_up_projection" times the value
-up-projection that follows the decode (DeepSeek-V3 shapes, bf16 weights).
+up-projection that follows the decode (DeepSeek-V3 shapes, bf16 weights); "context_merge" the
+log-sum-exp merge of four decode results over disjoint context parts (headline shapes).
 """
 
 from __future__ import annotations
@@ -338,6 +339,41 @@ def time_value_projection(steps: int, warmup: int, flush: bool, batch=32, heads=
             "bound": "hbm"}
 
 
+def time_context_merge(steps: int, warmup: int, flush: bool, parts=4, batch=32, heads=128, d_latent=512):
+    """tpla_merge_context_parts timed on its own (events around each call): the results of `parts`
+    decode calls over disjoint context parts at the headline shapes (G = 1), against its
+    algorithmic bytes: every part's output and log-sum-exp read once, the result written once."""
+    import torch
+
+    from mla_latent_kv_13_amd import binding, inputs
+
+    out_p, lse_p = inputs.make_context_parts(3, parts=parts, batch=batch, heads=heads, d_latent=d_latent,
+                                             shard_count=1, empty=0.0)
+    op = torch.from_numpy(out_p).to("cuda:0")
+    lp = torch.from_numpy(lse_p).to("cuda:0")
+    out = torch.empty((batch, heads, d_latent), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((batch, 1, heads), dtype=torch.float32, device="cuda:0")
+    flush_buf = _flush_buffer() if flush else None
+    for _ in range(warmup):
+        binding.tpla_merge_context_parts(op, lp, 1, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        if flush_buf is not None:
+            flush_buf.sum()
+        e[0].record()
+        binding.tpla_merge_context_parts(op, lp, 1, out=out, lse=lse)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
+    nbytes = (parts + 1) * batch * heads * d_latent * 4 + (parts + 1) * batch * heads * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del op, lp, out, lse
+    return {"shape": {"parts": parts, "batch": batch, "heads": heads, "d_latent": d_latent, "shards": 1},
+            "ms_mean": ms, "algorithmic_bytes": nbytes, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
+            "bound": "hbm"}
+
+
 def streaming_bandwidth(steps: int = 10):
     """What plain streaming reaches on this card with the runtime's own kernels: a
     device-to-device copy of 1 GiB (1 GiB read plus 1 GiB written), and a full reduction of a
@@ -496,6 +532,7 @@ def main():
         line["workloads"] = others
     if not args.headline_only:
         line["value_up_projection"] = time_value_projection(args.extra_steps, args.warmup, not args.no_flush)
+        line["context_merge"] = time_context_merge(args.extra_steps, args.warmup, not args.no_flush)
         line["achievable_streaming"] = streaming_bandwidth()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_case)

@@ -196,6 +196,30 @@ int32_t mla_decode_absorbed(const tpla_cache_desc_t* desc, const void* cache,
                             float* out, float* lse, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Merge of decode results over disjoint parts of each sequence's context, the
+ * exact context-parallel alternative to slicing the latent ([FR] Directions under
+ * investigation: context/sequence parallelism, a sequence split with a
+ * log-sum-exp merge): each part (say one device's tokens of every sequence) is
+ * decoded on its own with tpla_decode_sharded, and this call combines the P
+ * results into the result over the whole context.
+ *   transform, num_shards, shard_begin, shard_count: as passed to the decode calls
+ *   out_parts  device, fp32 [parts, batch, heads, d_latent]: their `out`
+ *   lse_parts  device, fp32 [parts, batch, shard_count, heads]: their `lse`
+ *   out        device, fp32 [batch, heads, d_latent], fully overwritten
+ *   lse        device, fp32 [batch, shard_count, heads] or NULL
+ * For each b, h and computed shard s (local index i), with y_p = H out_p under
+ * the Hadamard transform (H is its own inverse) and y_p = out_p otherwise:
+ *   lse_i = log sum_p exp(lse_p,i),   y[s*w:(s+1)*w] = sum_p exp(lse_p,i - lse_i) y_p[s*w:(s+1)*w]
+ * and out = H y (or y), zeros in the columns of shards not computed before the
+ * rotation.  Parts with lse = -inf add nothing; a shard with no tokens in any
+ * part gives 0 and -inf.  Limits: d_latent <= 1024, shard_count <= 64,
+ * batch <= 65535; batch or heads 0 is a no-op.  Alignment: out_parts and out
+ * 16 bytes, lse_parts and lse 4 bytes.  No workspace. */
+int32_t tpla_merge_context_parts(int32_t transform, int32_t num_shards, int32_t shard_begin,
+                                 int32_t shard_count, int32_t parts, int32_t batch, int32_t heads,
+                                 int32_t d_latent, const float* out_parts, const float* lse_parts,
+                                 float* out, float* lse, void* stream);
+
 /* Value up-projection of a decode result: with the key up-projection absorbed
  * into the query, attention runs in latent space and each head's value rows of
  * kv_b_proj are applied after it ([REV] referee report, significance: matrix

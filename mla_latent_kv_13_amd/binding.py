@@ -27,7 +27,7 @@ SCHEDULES = {"auto": 0, "chunked": 1, "balanced": 2}
 
 EXPORTED = ["tpla_abi_version", "tpla_status_string", "tpla_last_error", "tpla_workspace_size",
             "latent_cache_append", "tpla_decode_sharded", "tpla_decode_sharded_ex", "mla_decode_absorbed",
-            "tpla_value_up_projection"]
+            "tpla_value_up_projection", "tpla_merge_context_parts"]
 
 
 class TplaError(RuntimeError):
@@ -96,6 +96,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mla_decode_absorbed.restype = _I32
     lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.tpla_merge_context_parts.restype = _I32
+    lib.tpla_merge_context_parts.argtypes = [_I32] * 8 + [_P, _P, _P, _P, _P]
     lib.tpla_value_up_projection.restype = _I32
     lib.tpla_value_up_projection.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P]
     _LIB = lib
@@ -240,3 +242,25 @@ def tpla_value_up_projection(o: torch.Tensor, w_uv: torch.Tensor, out_v: torch.T
     _check(lib.tpla_value_up_projection(w_dtype, _ptr(o), _ptr(w_uv), batch, heads, d_latent, d_v, _ptr(out_v),
                                         _stream(stream)))
     return out_v
+
+
+def tpla_merge_context_parts(out_parts: torch.Tensor, lse_parts: torch.Tensor, num_shards: int,
+                             shard_begin: int = 0, transform: str = "identity", out: torch.Tensor | None = None,
+                             lse: torch.Tensor | None = None, want_lse: bool = True, stream=None):
+    """Merge P decode results over disjoint context parts: out_parts fp32 [P, B, H, d_latent],
+    lse_parts fp32 [P, B, n, H] -> (out [B, H, d_latent], lse [B, n, H] or None)."""
+    if out_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("out_parts and lse_parts must be fp32")
+    parts, batch, heads, d_latent = (int(x) for x in out_parts.shape)
+    shard_count = int(lse_parts.shape[2])
+    if tuple(lse_parts.shape) != (parts, batch, shard_count, heads):
+        raise ValueError("lse_parts must be [parts, batch, shard_count, heads]")
+    if out is None:
+        out = torch.empty((batch, heads, d_latent), dtype=torch.float32, device=out_parts.device)
+    if lse is None and want_lse:
+        lse = torch.empty((batch, shard_count, heads), dtype=torch.float32, device=out_parts.device)
+    lib = load_library()
+    _check(lib.tpla_merge_context_parts(TRANSFORMS[transform], num_shards, shard_begin, shard_count, parts, batch,
+                                        heads, d_latent, _ptr(out_parts), _ptr(lse_parts), _ptr(out), _ptr(lse),
+                                        _stream(stream)))
+    return out, lse

@@ -331,6 +331,45 @@ int32_t latent_cache_append(const tpla_cache_desc_t* desc, void* cache, const vo
   return ok();
 }
 
+int32_t tpla_merge_context_parts(int32_t transform, int32_t num_shards, int32_t shard_begin, int32_t shard_count,
+                                 int32_t parts, int32_t batch, int32_t heads, int32_t d_latent,
+                                 const float* out_parts, const float* lse_parts, float* out, float* lse,
+                                 void* stream) {
+  if (transform != TPLA_LATENT_IDENTITY && transform != TPLA_LATENT_WHT)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "unknown latent transform %d", transform);
+  if (parts < 1 || batch < 0 || heads < 0 || d_latent < 1)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "parts >= 1, batch and heads >= 0, d_latent >= 1 required");
+  if (num_shards < 1 || d_latent % num_shards != 0)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "num_shards=%d must be >= 1 and divide d_latent=%d", num_shards, d_latent);
+  if (shard_begin < 0 || shard_count < 1 || shard_begin + shard_count > num_shards)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "shard range [%d, %d) outside [0, %d)", shard_begin, shard_begin + shard_count,
+                num_shards);
+  if (d_latent > 1024 || shard_count > 64) return fail(TPLA_ERR_UNSUPPORTED, "d_latent <= 1024 and shard_count <= 64");
+  if (transform == TPLA_LATENT_WHT && (d_latent & (d_latent - 1)) != 0)
+    return fail(TPLA_ERR_UNSUPPORTED, "the Hadamard transform needs d_latent a power of two <= 1024");
+  if (batch > 65535) return fail(TPLA_ERR_UNSUPPORTED, "batch <= 65535");
+  if (batch == 0 || heads == 0) return ok();
+  if (!out_parts || !lse_parts || !out) return fail(TPLA_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
+  if (!aligned(out_parts, 16) || !aligned(out, 16) || !aligned(lse_parts, 4) || (lse && !aligned(lse, 4)))
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "out_parts and out must be 16-byte aligned, lse_parts and lse 4-byte");
+  tpla::ContextMergeLaunch L{};
+  L.out_parts = out_parts;
+  L.lse_parts = lse_parts;
+  L.parts = parts;
+  L.batch = batch;
+  L.heads = heads;
+  L.d_latent = d_latent;
+  L.num_shards = num_shards;
+  L.shard_begin = shard_begin;
+  L.shard_count = shard_count;
+  L.wht = transform == TPLA_LATENT_WHT ? 1 : 0;
+  L.out = out;
+  L.lse = lse;
+  const hipError_t e = tpla::launch_context_merge(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "context merge launch");
+  return ok();
+}
+
 int32_t tpla_value_up_projection(int32_t w_dtype, const float* o, const void* w_uv, int32_t batch, int32_t heads,
                                  int32_t d_latent, int32_t d_v, float* out_v, void* stream) {
   if (w_dtype != TPLA_F32 && w_dtype != TPLA_BF16) return fail(TPLA_ERR_UNSUPPORTED, "w_dtype %d is not fp32 or bf16", w_dtype);

@@ -52,6 +52,18 @@ struct MergeLaunch {
 
 // dtype: 0 = fp32, 1 = bf16 storage.
 hipError_t launch_decode_generic(const DecodeLaunch& a, int dtype, hipStream_t stream);
+// Decode results over P disjoint parts of each context, merged by log-sum-exp.
+struct ContextMergeLaunch {
+  const float* out_parts;  // [parts, batch, heads, d_latent]
+  const float* lse_parts;  // [parts, batch, shard_count, heads]
+  int parts, batch, heads, d_latent;
+  int num_shards, shard_begin, shard_count;
+  int wht;
+  float* out;  // [batch, heads, d_latent]
+  float* lse;  // [batch, shard_count, heads] or null
+};
+hipError_t launch_context_merge(const ContextMergeLaunch& a, hipStream_t stream);
+
 // Returns hipErrorInvalidValue when no MFMA tile covers the shape (checked by mfma_supported first).
 bool mfma_supported(int w, int d_rope, int heads);
 hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t stream);

@@ -270,6 +270,104 @@ rows_done:
   }
 }
 
+// Context merge: decode results over P disjoint parts of every sequence's context combined by
+// log-sum-exp into the result over the whole context (feature request on latent-cache sharding,
+// "Directions under investigation": context parallelism, a sequence split with a log-sum-exp
+// merge).  One wave per (sequence, head).  Lane i < shard_count gathers local shard i's
+// log-sum-exps over the parts: lse_i = M + ln sum_p e^(lse_p,i - M).  Then, part by part, the
+// latent row y_p (= H out_p under the Hadamard transform, H being its own inverse) is added with
+// the weight e^(lse_p,i - lse_i) of each column's shard; the sum is rotated back (out = H y).
+// Parts with lse = -inf add nothing; a shard with no tokens anywhere gives 0 and -inf.  The rows
+// of the first PB parts are requested before the log-sum-exps are combined, and PB parts at a
+// time after that (indices clamped to the last part, branches only around the arithmetic).
+// V > 0: V consecutive values per lane (d_latent = 64 V, or V = 1 below 64), rotated when WHT;
+// V = 0: value lane + 64 r in register r (other widths, no rotation).
+template <int V, bool WHT>
+__global__ __launch_bounds__(kThreads) void context_merge_kernel(ContextMergeLaunch a) {
+  constexpr int R = V > 0 ? V : kMaxLatent / 64;  // values a lane holds
+  constexpr int PB = 4;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kMergeWaves + wv, b = blockIdx.y;
+  if (h >= a.heads) return;  // the rest of this kernel is wave-local
+  const int n = a.d_latent, sc = a.shard_count, w = n / a.num_shards;
+  const int64_t bh = static_cast<int64_t>(b) * a.heads + h;
+  const int64_t part_stride = static_cast<int64_t>(a.batch) * a.heads * n;
+  const int64_t lse_stride = static_cast<int64_t>(a.batch) * sc * a.heads;
+  const bool mine = lane < sc;  // this lane holds local shard `lane`
+  const int64_t lse_at = (static_cast<int64_t>(b) * sc + (mine ? lane : 0)) * a.heads + h;
+  const bool on = V > 0 ? lane < n / V : true;
+  float x[PB][R];
+  float lp[PB];
+  auto load = [&](int p0) {
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int p = min(p0 + k, a.parts - 1);
+      const float* src = a.out_parts + p * part_stride + bh * n;
+      if constexpr (V > 0) {
+        const Pack<float, V> pk = reinterpret_cast<const Pack<float, V>*>(src)[on ? lane : 0];
+#pragma unroll
+        for (int r = 0; r < V; ++r) x[k][r] = pk.v[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[k][r] = src[min(lane + 64 * r, n - 1)];
+      }
+      lp[k] = a.lse_parts[p * lse_stride + lse_at];
+    }
+  };
+  load(0);
+  float m = -INFINITY;
+  for (int p0 = 0; p0 < a.parts; p0 += PB) {
+    float l[PB];
+#pragma unroll
+    for (int k = 0; k < PB; ++k) l[k] = a.lse_parts[min(p0 + k, a.parts - 1) * lse_stride + lse_at];
+#pragma unroll
+    for (int k = 0; k < PB; ++k) m = fmaxf(m, l[k]);  // a repeated last part does not change the maximum
+  }
+  float z = 0.f;
+  if (m != -INFINITY)
+    for (int p = 0; p < a.parts; ++p) z += expf(a.lse_parts[p * lse_stride + lse_at] - m);
+  const float lse_i = m != -INFINITY ? m + logf(z) : -INFINITY;
+  if (a.lse != nullptr && mine) a.lse[lse_at] = lse_i;
+
+  // local shard of each value this lane holds (-1: a shard that was not computed, or padding)
+  int shard_of[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = V > 0 ? V * lane + r : lane + 64 * r;
+    const int i = j < n ? j / w - a.shard_begin : -1;
+    shard_of[r] = i >= 0 && i < sc ? i : -1;
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  for (int p0 = 0; p0 < a.parts; p0 += PB) {
+    if (p0 > 0) load(p0);
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      if (p0 + k >= a.parts) break;
+      if constexpr (WHT) wave_wht(x[k], n, lane);  // y_p = H out_p
+      const float wl = mine && lse_i != -INFINITY ? expf(lp[k] - lse_i) : 0.f;  // weight of part p for shard `lane`
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float wt = __shfl(wl, shard_of[r] >= 0 ? shard_of[r] : 0);
+        if (shard_of[r] >= 0) acc[r] = fmaf(wt, x[k][r], acc[r]);
+      }
+    }
+  }
+  float* dst = a.out + bh * n;
+  if constexpr (V > 0) {
+    if constexpr (WHT) wave_wht(acc, n, lane);  // out = H y
+    Pack<float, V> pk;
+#pragma unroll
+    for (int r = 0; r < V; ++r) pk.v[r] = acc[r];
+    if (on) reinterpret_cast<Pack<float, V>*>(dst)[lane] = pk;
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (lane + 64 * r < n) dst[lane + 64 * r] = acc[r];
+  }
+}
+
 // One wave per query row, four rows per block: V consecutive values per lane, rotated in registers.
 template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void rotate_query_kernel(const T* __restrict__ q, int rows, int d_latent,
@@ -369,6 +467,34 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
   else if (pr == 2) kern = steps == 4 ? merge_kernel<4, 1, 2, 4> : steps == 8 ? merge_kernel<4, 1, 2, 8> : merge_kernel<4, 1, 2, 16>;
   else kern = steps == 4 ? merge_kernel<4, 1, 4, 4> : steps == 8 ? merge_kernel<4, 1, 4, 8> : merge_kernel<4, 1, 4, 16>;
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_context_merge(const ContextMergeLaunch& a, hipStream_t stream) {
+  if (a.d_latent > kMaxLatent || a.shard_count > 64) return hipErrorInvalidValue;
+  if (a.wht && (a.d_latent & (a.d_latent - 1)) != 0) return hipErrorInvalidValue;
+  if (a.batch == 0 || a.heads == 0) return hipSuccess;
+  const dim3 grid((a.heads + kMergeWaves - 1) / kMergeWaves, a.batch);
+  // the packed layout needs d_latent = 64 V (V a power of two), or V = 1 below 64 (rotated rows only)
+  const int v = a.d_latent <= 64 ? (a.wht ? 1 : (a.d_latent == 64 ? 1 : 0)) : a.d_latent / 64;
+  const bool packed = v > 0 && (v & (v - 1)) == 0 && (a.d_latent <= 64 || a.d_latent % 64 == 0);
+#define TPLA_CM(VV)                                                                             \
+  if (a.wht)                                                                                    \
+    hipLaunchKernelGGL((context_merge_kernel<VV, true>), grid, dim3(kThreads), 0, stream, a);   \
+  else                                                                                          \
+    hipLaunchKernelGGL((context_merge_kernel<VV, false>), grid, dim3(kThreads), 0, stream, a)
+  if (!packed) {
+    hipLaunchKernelGGL((context_merge_kernel<0, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    switch (v) {
+      case 1: TPLA_CM(1); break;
+      case 2: TPLA_CM(2); break;
+      case 4: TPLA_CM(4); break;
+      case 8: TPLA_CM(8); break;
+      default: TPLA_CM(16); break;
+    }
+  }
+#undef TPLA_CM
   return hipGetLastError();
 }
 

@@ -15,6 +15,10 @@ Recipe (one generator per tensor, ``np.random.default_rng([case_seed, tensor_id]
   tensor 5  context lengths, integers uniform in [lo, hi] inclusive
   tensor 6  page permutation for the paged layout
 
+Context-merge inputs (``make_context_parts``, its own seed): tensor 0 the parts' outputs
+[P, B, H, d_c] (float32 normals), tensor 1 their log-sum-exps [P, B, n, H] (normals times 3),
+tensor 2 which of those are -inf (a part with no tokens), each with probability ``empty``.
+
 Value up-projection inputs (``make_value_projection``, its own seed): tensor 0 the latent-frame
 attention output o [B, H, d_c] (float32 normals), tensor 1 the per-head value weights
 W_UV [H, d_v, d_c], normals scaled by 1/sqrt(d_c) (the spread of a trained projection's
@@ -228,3 +232,13 @@ def make_value_projection(seed: int, *, batch: int, heads: int, d_latent: int, d
     w = np.random.default_rng([seed, 1]).standard_normal((heads, d_v, d_latent), dtype=np.float32)
     w = (w * np.float32(1.0 / math.sqrt(d_latent))).astype(np.float32)
     return o, _to_dtype(w, dtype)
+
+
+def make_context_parts(seed: int, *, parts: int, batch: int, heads: int, d_latent: int, shard_count: int,
+                       empty: float = 0.2):
+    """Seeded (out_parts [P, B, H, d_c], lse_parts [P, B, n, H]) float32 for the context merge."""
+    out = np.random.default_rng([seed, 0]).standard_normal((parts, batch, heads, d_latent), dtype=np.float32)
+    lse = np.random.default_rng([seed, 1]).standard_normal((parts, batch, shard_count, heads), dtype=np.float32)
+    lse = (lse * np.float32(3.0)).astype(np.float32)
+    lse[np.random.default_rng([seed, 2]).random(lse.shape) < empty] = -np.inf
+    return out, lse

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("latent_cache_append", "tpla_decode_sharded", "mla_decode_absorbed", "tpla_workspace_size",
-                     "tpla_value_up_projection"):
+                     "tpla_value_up_projection", "tpla_merge_context_parts"):
         assert required in names
     assert set(names) == set(binding.EXPORTED)
 
@@ -168,3 +168,38 @@ def test_up_projection_empty_is_a_no_op(lib):
     # nothing is enqueued, so no device is touched: fine without a GPU
     assert _up_raw(lib, batch=0, o=0, w=0, out=0)[0] == 0
     assert _up_raw(lib, heads=0, o=0, w=0, out=0)[0] == 0
+
+
+def _merge_raw(lib, **kw):
+    """tpla_merge_context_parts with fake (never dereferenced) device addresses; only for
+    arguments that validation settles before anything is enqueued."""
+    a = dict(transform=0, G=2, s0=0, n=2, parts=3, batch=4, heads=8, d=512, op=0x10000, lp=0x20000, out=0x30000,
+             lse=0x40000)
+    a.update(kw)
+    p = ctypes.c_void_p
+    st = lib.tpla_merge_context_parts(a["transform"], a["G"], a["s0"], a["n"], a["parts"], a["batch"], a["heads"],
+                                      a["d"], p(a["op"] or None), p(a["lp"] or None), p(a["out"] or None),
+                                      p(a["lse"] or None), None)
+    return st, lib.tpla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(transform=5), 1),
+    (dict(parts=0), 1),
+    (dict(G=3), 1),                 # 3 does not divide 512
+    (dict(s0=1, n=2), 1),           # shard range beyond G
+    (dict(d=2048, G=2), 2),
+    (dict(G=128, n=128), 2),        # more than 64 shards in one call
+    (dict(transform=1, d=96, G=1, n=1), 2),  # Hadamard needs a power of two
+    (dict(op=0), 1),
+    (dict(out=0x30008), 1),         # misaligned output
+    (dict(batch=70000), 2),
+])
+def test_context_merge_validation_before_launch(lib, kw, status):
+    st, msg = _merge_raw(lib, **kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_context_merge_empty_is_a_no_op(lib):
+    assert _merge_raw(lib, batch=0, op=0, lp=0, out=0, lse=0)[0] == 0
