@@ -18,4 +18,5 @@ from .tpla_oracle import (  # noqa: F401
     mla_unabsorbed_bruteforce,
     value_up_projection,
     merge_context_parts,
+    rms_normalize,
 )

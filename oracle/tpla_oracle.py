@@ -69,6 +69,7 @@ __all__ = [
     "mla_unabsorbed_bruteforce",
     "value_up_projection",
     "merge_context_parts",
+    "rms_normalize",
 ]
 
 
@@ -136,30 +137,53 @@ def _store(values: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def latent_cache_append(pool, rows, slots, d_latent: int, transform: str, dtype: str) -> np.ndarray:
+def rms_normalize(values, num_slices: int, eps: float) -> np.ndarray:
+    """RMSNorm with unit gain over each of ``num_slices`` equal slices of the last axis:
+    x_s / sqrt(mean(x_s ** 2) + eps).  One slice is the whole-latent norm of MLA's
+    kv_a_layernorm; G slices are the shard-local norm a device holding only its slice
+    can apply ([REV] key_machinery: Condition 1, shard RMS norms proportional to the
+    global norm; referee report: Proposition 1, RMSNorm under orthogonal transforms;
+    [FR] Summary: the reparameterised kv_a_layernorm).  Unit gain: learned weights are
+    not part of this path."""
+    values = np.asarray(values, dtype=np.float64)
+    d = values.shape[-1]
+    if d % num_slices != 0:
+        raise ValueError("the latent width must split evenly into the slices")
+    w = d // num_slices
+    out = np.empty_like(values)
+    for s in range(num_slices):
+        part = values[..., s * w:(s + 1) * w]
+        out[..., s * w:(s + 1) * w] = part / np.sqrt(np.mean(part * part, axis=-1, keepdims=True) + eps)
+    return out
+
+
+def latent_cache_append(pool, rows, slots, d_latent: int, transform: str, dtype: str,
+                        norm_slices: int = 0, eps: float = 0.0) -> np.ndarray:
     """Write new cache rows into a copy of ``pool`` and return it (float64).
 
     Row i goes to flat row ``slots[i]`` (= page * page_size + offset).  With
     ``transform == "wht"`` the latent part is rotated, x_lat <- H x_lat, before
     it is stored in the cache dtype (readings A5, A7); the rope part is stored
-    unchanged.  Follows [FR] Directions (orthogonal reparameterisation of the
-    latent before slicing) and [ABS].
+    unchanged.  With ``norm_slices`` >= 1 the (rotated) latent is then
+    RMS-normalised with unit gain over that many equal slices (1: the whole
+    latent), before the rounding; the rope part is not normalised.  Follows
+    [FR] Directions (orthogonal reparameterisation of the latent before
+    slicing), [ABS], and for the normalisation [REV] (Condition 1,
+    Proposition 1).
     """
     pool = np.array(pool, dtype=np.float64, copy=True)
     num_pages, page_size, width = pool.shape
     flat = pool.reshape(num_pages * page_size, width)
     rows = np.asarray(rows, dtype=np.float64)
-    if transform == "wht":
-        hmat = hadamard(d_latent)
-        for i, slot in enumerate(np.asarray(slots).tolist()):
-            lat = hmat @ rows[i, :d_latent]
-            flat[slot, :d_latent] = _store(lat, dtype)
-            flat[slot, d_latent:] = rows[i, d_latent:]
-    elif transform == "identity":
-        for i, slot in enumerate(np.asarray(slots).tolist()):
-            flat[slot] = rows[i]
-    else:
+    if transform not in ("wht", "identity"):
         raise ValueError(f"unknown transform {transform!r}")
+    hmat = hadamard(d_latent) if transform == "wht" else None
+    for i, slot in enumerate(np.asarray(slots).tolist()):
+        lat = hmat @ rows[i, :d_latent] if hmat is not None else rows[i, :d_latent]
+        if norm_slices:
+            lat = rms_normalize(lat, norm_slices, eps)
+        flat[slot, :d_latent] = _store(lat, dtype) if (hmat is not None or norm_slices) else rows[i, :d_latent]
+        flat[slot, d_latent:] = rows[i, d_latent:]
     return flat.reshape(num_pages, page_size, width)
 
 

@@ -473,6 +473,58 @@ def pin_append(orc):
     assert np.array_equal(rot[slots, d_c:], rows[:, d_c:])
 
 
+def pin_p14_rms_norm_in_append(orc):
+    """RMSNorm with unit gain in the append ([REV] referee report: Proposition 1,
+    RMSNorm under orthogonal transforms; key_machinery: Condition 1, shard RMS
+    norms proportional to the global norm):
+    * Proposition 1: rotating then normalising the whole latent stores exactly
+      H applied to the normalised row (computed here with scipy's Hadamard);
+    * each slice of a shard-local norm has mean square m / (m + eps), m the mean
+      square of that slice of the rotated row (closed form);
+    * when every slice has the same norm (Condition 1 holding exactly), the
+      shard-local norm equals the whole-latent norm;
+    * with eps = 0 the norm does not depend on the row's scale;
+    * the rope part is stored unchanged, and bf16 storage rounds the normalised
+      value."""
+    rng = np.random.default_rng(141)
+    d_c, d_r, n = 64, 8, 6
+    rows = rng.standard_normal((n, d_c + d_r)) * np.linspace(0.5, 3.0, d_c + d_r)
+    pool = np.full((2, 4, d_c + d_r), np.nan)
+    slots = np.arange(n)
+    hmat = scipy.linalg.hadamard(d_c).astype(np.float64) / math.sqrt(d_c)
+
+    glob = orc.latent_cache_append(pool, rows, slots, d_c, "wht", "f64", norm_slices=1).reshape(8, -1)[slots]
+    x = rows[:, :d_c]
+    want = (x / np.sqrt(np.mean(x * x, axis=1, keepdims=True))) @ hmat.T
+    assert np.max(np.abs(glob[:, :d_c] - want)) <= 1e-13, "P14 Proposition 1"
+    assert np.array_equal(glob[:, d_c:], rows[:, d_c:]), "P14 rope"
+
+    eps = 1e-2
+    for transform in ("identity", "wht"):
+        loc = orc.latent_cache_append(pool, rows, slots, d_c, transform, "f64", norm_slices=4,
+                                      eps=eps).reshape(8, -1)[slots]
+        base = x @ hmat.T if transform == "wht" else x
+        for s in range(4):
+            sl = slice(16 * s, 16 * (s + 1))
+            m = np.mean(base[:, sl] ** 2, axis=1)
+            got = np.mean(loc[:, sl] ** 2, axis=1)
+            assert np.max(np.abs(got - m / (m + eps))) <= 1e-13, ("P14 slice mean square", transform, s)
+
+    u = rng.standard_normal(16)
+    eq = np.concatenate([u, -u[::-1], np.roll(u, 3), u * np.tile([1.0, -1.0], 8)])  # four slices, one norm
+    eq_rows = np.concatenate([np.stack([eq, 2.5 * eq]), rng.standard_normal((2, d_r))], axis=1)
+    a = orc.latent_cache_append(pool, eq_rows, [0, 1], d_c, "identity", "f64", norm_slices=4).reshape(8, -1)[:2]
+    b = orc.latent_cache_append(pool, eq_rows, [0, 1], d_c, "identity", "f64", norm_slices=1).reshape(8, -1)[:2]
+    assert np.max(np.abs(a - b)) <= 1e-14, "P14 Condition 1 exact"
+    assert np.max(np.abs(a[0, :d_c] - a[1, :d_c])) <= 1e-14, "P14 scale invariance"
+
+    bf = orc.latent_cache_append(pool, rows, slots, d_c, "wht", "bf16", norm_slices=2, eps=1e-6).reshape(8, -1)[slots]
+    exact = orc.latent_cache_append(pool, rows, slots, d_c, "wht", "f64", norm_slices=2, eps=1e-6).reshape(8, -1)[slots]
+    ref = torch.from_numpy(exact[:, :d_c].astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    ulp = np.ldexp(1.0, np.frexp(ref)[1] - 8)
+    assert np.all(np.abs(bf[:, :d_c] - ref) <= ulp) and np.mean(bf[:, :d_c] == ref) > 0.99, "P14 rounding"
+
+
 # ---------------------------------------------------------------- bf16 and golden fixtures
 def pin_bf16_rne(orc):
     """Round-to-nearest-even to bfloat16 agrees with torch's conversion on
@@ -534,6 +586,7 @@ ALL_PINS = [
     pin_p10_context_split_merge,
     pin_paged_gather,
     pin_append,
+    pin_p14_rms_norm_in_append,
     pin_bf16_rne,
     pin_golden_hand_cases,
 ]

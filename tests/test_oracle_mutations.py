@@ -41,6 +41,12 @@ MUTATIONS = {
     "merge_no_unrotation": ("ys = [out_parts[p, b, h] @ hmat if hmat is not None else out_parts[p, b, h] for p in range(parts)]",
                             "ys = [out_parts[p, b, h] for p in range(parts)]"),
     "merge_lse_without_max": ("lse[b, i, h] = m + np.log(z)", "lse[b, i, h] = np.log(z)"),
+    "norm_sum_not_mean": ("np.mean(part * part, axis=-1, keepdims=True) + eps", "np.sum(part * part, axis=-1, keepdims=True) + eps"),
+    "norm_ignores_slices": ("lat = rms_normalize(lat, norm_slices, eps)", "lat = rms_normalize(lat, 1, eps)"),
+    "norm_before_rotation": ("lat = hmat @ rows[i, :d_latent] if hmat is not None else rows[i, :d_latent]",
+                             "lat = rows[i, :d_latent]\n        lat = rms_normalize(lat, norm_slices, eps) if norm_slices else lat\n        lat = hmat @ lat if hmat is not None else lat"),
+    "norm_eps_outside_root": ("part / np.sqrt(np.mean(part * part, axis=-1, keepdims=True) + eps)",
+                              "part / (np.sqrt(np.mean(part * part, axis=-1, keepdims=True)) + eps)"),
     "empty_lse_zero": ("lse = np.full((batch, shard_count, heads), -np.inf, dtype=np.float64)",
                        "lse = np.full((batch, shard_count, heads), 0.0, dtype=np.float64)"),
 }
