@@ -21,7 +21,8 @@ ragged contexts) are reported in "workloads" unless --headline-only is given; th
 contiguous TPLA workloads also carry "per_device_share": the call of one shard (what one
 of G devices would read and compute) and the G = 1 call over the same cache.  "append"
 times latent_cache_append on its own on the paged Hadamard workload's rows: the whole
-cache and one row per sequence, rotated and plain; "value_up_projection" times the value
+cache and one row per sequence, rotated and plain (and rotated with a per-shard RMS norm);
+"value_up_projection" times the value
 up-projection that follows the decode (DeepSeek-V3 shapes, bf16 weights); "context_merge" the
 log-sum-exp merge of four decode results over disjoint context parts (headline shapes).
 """
@@ -278,16 +279,22 @@ def time_append(w: Workload, steps: int, warmup: int, flush: bool):
     plain = binding.Desc(c.dtype, c.d_latent, c.d_rope, c.page_size, c.num_pages, c.max_pages_per_seq, "identity")
     scratch = torch.empty_like(w.pool)
 
-    def timed(desc, pool, r, sl, n_steps):
+    def timed(desc, pool, r, sl, n_steps, norm=0):
+        def call():
+            if norm:
+                binding.latent_cache_append_normed(desc, pool, r, sl, norm, 1e-6)
+            else:
+                binding.latent_cache_append(desc, pool, r, sl)
+
         for _ in range(warmup):
-            binding.latent_cache_append(desc, pool, r, sl)
+            call()
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_steps)]
         for e in ev:
             if flush_buf is not None:
                 flush_buf.sum()
             e[0].record()
-            binding.latent_cache_append(desc, pool, r, sl)
+            call()
             e[1].record()
         torch.cuda.synchronize()
         ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
@@ -301,6 +308,10 @@ def time_append(w: Workload, steps: int, warmup: int, flush: bool):
             continue
         res[name] = {"whole_cache": timed(desc, pool, rows, slots, max(3, steps // 3)),
                      "one_row_per_sequence": timed(desc, pool, step_rows, step_slots, steps)}
+    # rotated and normalised per shard slice (into the second pool: the decode inputs stay as they were)
+    rdesc = binding.Desc(c.dtype, c.d_latent, c.d_rope, c.page_size, c.num_pages, c.max_pages_per_seq, "wht")
+    res["wht_rms_norm_per_shard_into_second_pool"] = {
+        "norm_slices": c.shards, "whole_cache": timed(rdesc, scratch, rows, slots, max(3, steps // 3), c.shards)}
     del rows, slots, step_rows, step_slots, scratch
     torch.cuda.empty_cache()
     return res

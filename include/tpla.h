@@ -196,6 +196,21 @@ int32_t mla_decode_absorbed(const tpla_cache_desc_t* desc, const void* cache,
                             float* out, float* lse, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* latent_cache_append with an RMS normalisation of the latent, unit gain ([REV]
+ * referee report: Proposition 1, RMSNorm under orthogonal transforms;
+ * key_machinery: Condition 1, shard RMS norms proportional to the global norm;
+ * [FR] Summary: the reparameterised kv_a_layernorm).  After the optional Hadamard
+ * rotation (desc->transform) and before the rounding to the cache dtype, the
+ * latent x (d_latent values) is split into norm_slices equal slices and each
+ * slice becomes x_s / sqrt(mean(x_s^2) + eps): norm_slices = 1 is the
+ * whole-latent norm, G the shard-local norm a device holding only its slice can
+ * apply.  The rope part is stored unchanged.  Needs d_latent a power of two
+ * <= 1024, 1 <= norm_slices <= 64 dividing d_latent, eps finite and >= 0;
+ * everything else as latent_cache_append.  Learned gains are not applied. */
+int32_t latent_cache_append_normed(const tpla_cache_desc_t* desc, void* cache, const void* rows,
+                                   const int64_t* slots, int64_t n, int32_t norm_slices, float eps,
+                                   void* stream);
+
 /* Merge of decode results over disjoint parts of each sequence's context, the
  * exact context-parallel alternative to slicing the latent ([FR] Directions under
  * investigation: context/sequence parallelism, a sequence split with a

@@ -27,7 +27,7 @@ SCHEDULES = {"auto": 0, "chunked": 1, "balanced": 2}
 
 EXPORTED = ["tpla_abi_version", "tpla_status_string", "tpla_last_error", "tpla_workspace_size",
             "latent_cache_append", "tpla_decode_sharded", "tpla_decode_sharded_ex", "mla_decode_absorbed",
-            "tpla_value_up_projection", "tpla_merge_context_parts"]
+            "tpla_value_up_projection", "tpla_merge_context_parts", "latent_cache_append_normed"]
 
 
 class TplaError(RuntimeError):
@@ -96,6 +96,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mla_decode_absorbed.restype = _I32
     lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.latent_cache_append_normed.restype = _I32
+    lib.latent_cache_append_normed.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, ctypes.c_int64, _I32,
+                                               ctypes.c_float, _P]
     lib.tpla_merge_context_parts.restype = _I32
     lib.tpla_merge_context_parts.argtypes = [_I32] * 8 + [_P, _P, _P, _P, _P]
     lib.tpla_value_up_projection.restype = _I32
@@ -165,6 +168,17 @@ def latent_cache_append(desc: Desc, cache: torch.Tensor, rows: torch.Tensor, slo
     cdesc = desc.c()
     _check(lib.latent_cache_append(ctypes.byref(cdesc), _ptr(cache), _ptr(rows), _ptr(slots), int(slots.numel()),
                                    _stream(stream)))
+
+
+def latent_cache_append_normed(desc: Desc, cache: torch.Tensor, rows: torch.Tensor, slots: torch.Tensor,
+                               norm_slices: int, eps: float = 1e-6, stream=None) -> None:
+    """latent_cache_append with the latent RMS-normalised (unit gain) over norm_slices equal slices."""
+    if slots.dtype != torch.int64:
+        raise ValueError("slots must be int64")
+    lib = load_library()
+    cdesc = desc.c()
+    _check(lib.latent_cache_append_normed(ctypes.byref(cdesc), _ptr(cache), _ptr(rows), _ptr(slots),
+                                          int(slots.numel()), norm_slices, ctypes.c_float(eps), _stream(stream)))
 
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:

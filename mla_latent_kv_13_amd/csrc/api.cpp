@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -313,22 +314,45 @@ int32_t tpla_workspace_size(const tpla_cache_desc_t* desc, int32_t batch, int32_
   return ok();
 }
 
-int32_t latent_cache_append(const tpla_cache_desc_t* desc, void* cache, const void* rows, const int64_t* slots,
-                            int64_t n, void* stream) {
+namespace {
+
+int32_t append_impl(const tpla_cache_desc_t* desc, void* cache, const void* rows, const int64_t* slots, int64_t n,
+                    int32_t norm_slices, float eps, void* stream) {
   int32_t st = check_desc(desc);
   if (st != TPLA_OK) return st;
   if (n < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "n must be >= 0");
+  if (norm_slices < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "norm_slices must be >= 0");
+  if (norm_slices > 0) {
+    if (desc->d_latent % norm_slices != 0)
+      return fail(TPLA_ERR_INVALID_ARGUMENT, "norm_slices=%d must divide d_latent=%d", norm_slices, desc->d_latent);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(TPLA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    if (desc->d_latent > 1024 || (desc->d_latent & (desc->d_latent - 1)) != 0 || norm_slices > 64)
+      return fail(TPLA_ERR_UNSUPPORTED, "normalisation needs d_latent a power of two <= 1024 and norm_slices <= 64");
+  }
   if (n == 0) return ok();
   if (!cache || !rows || !slots) return fail(TPLA_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
   if (!aligned(cache, 16) || !aligned(rows, 16) || !aligned(slots, 8))
     return fail(TPLA_ERR_INVALID_ARGUMENT, "cache and rows must be 16-byte aligned, slots 8-byte aligned");
-  if (desc->transform == TPLA_LATENT_WHT && n > 0x7fffffffLL)
-    return fail(TPLA_ERR_UNSUPPORTED, "at most 2^31-1 rows per rotated append");
+  if ((desc->transform == TPLA_LATENT_WHT || norm_slices > 0) && n > 0x7fffffffLL)
+    return fail(TPLA_ERR_UNSUPPORTED, "at most 2^31-1 rows per rotated or normalised append");
   const hipError_t e = tpla::launch_append(cache, rows, slots, n, desc->d_latent, desc->d_rope,
                                            desc->dtype == TPLA_BF16 ? 1 : 0, desc->transform == TPLA_LATENT_WHT ? 1 : 0,
-                                           static_cast<hipStream_t>(stream));
+                                           norm_slices, eps, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return ok();
+}
+
+}  // namespace
+
+int32_t latent_cache_append(const tpla_cache_desc_t* desc, void* cache, const void* rows, const int64_t* slots,
+                            int64_t n, void* stream) {
+  return append_impl(desc, cache, rows, slots, n, 0, 0.f, stream);
+}
+
+int32_t latent_cache_append_normed(const tpla_cache_desc_t* desc, void* cache, const void* rows, const int64_t* slots,
+                                   int64_t n, int32_t norm_slices, float eps, void* stream) {
+  if (norm_slices < 1) return fail(TPLA_ERR_INVALID_ARGUMENT, "norm_slices must be >= 1");
+  return append_impl(desc, cache, rows, slots, n, norm_slices, eps, stream);
 }
 
 int32_t tpla_merge_context_parts(int32_t transform, int32_t num_shards, int32_t shard_begin, int32_t shard_count,

@@ -14,13 +14,16 @@ constexpr int kMaxLatent = 1024;
 constexpr int kRowsPerBlock = kThreads / 64;  // one wave per appended row
 
 // One wave per row at a time, the grid striding over the rows: lane l holds latent elements
-// V*l .. V*l+V-1 (V = d_latent / 64, or 1 with lanes >= d_latent idle), rotated in registers,
-// and rope-key piece l (16 bytes; the first 64 pieces), copied unchanged.  The next row's loads
-// are issued before this row is rotated (a wave's last prefetch re-reads row n - 1, unused).
-template <typename T, int V>
-__global__ __launch_bounds__(kThreads) void append_wht_kernel(T* __restrict__ cache, const T* __restrict__ rows,
+// V*l .. V*l+V-1 (V = d_latent / 64, or 1 with lanes >= d_latent idle), rotated in registers when
+// ROT, and rope-key piece l (16 bytes; the first 64 pieces), copied unchanged.  With norm_lanes > 0
+// the (rotated) latent is then RMS-normalised with unit gain over slices of norm_lanes * V values:
+// each slice's sum of squares is a reduction over the aligned group of lanes holding it, and the
+// slice is scaled by 1 / sqrt(mean square + eps).  The next row's loads are issued before this row
+// is processed (a wave's last prefetch re-reads row n - 1, unused).
+template <typename T, int V, bool ROT>
+__global__ __launch_bounds__(kThreads) void append_row_kernel(T* __restrict__ cache, const T* __restrict__ rows,
                                                                const int64_t* __restrict__ slots, int64_t n,
-                                                               int d_latent, int d_rope) {
+                                                               int d_latent, int d_rope, int norm_lanes, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kRowsPerBlock;
   int64_t i = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
@@ -30,6 +33,7 @@ __global__ __launch_bounds__(kThreads) void append_wht_kernel(T* __restrict__ ca
   const bool on = lane < lanes;
   const int pieces = d_rope * static_cast<int>(sizeof(T)) / 16;  // rope key in 16-byte pieces
   const bool rope_on = lane < pieces;
+  const float inv_w = norm_lanes > 0 ? 1.0f / static_cast<float>(norm_lanes * V) : 0.f;
   // every lane loads in bounds: idle lanes repeat piece 0 (of the latent when there is no rope)
   auto load = [&](int64_t r, Pack<T, V>& p, uint4& rk) {
     const T* src = rows + r * D;
@@ -47,7 +51,16 @@ __global__ __launch_bounds__(kThreads) void append_wht_kernel(T* __restrict__ ca
     float x[V];
 #pragma unroll
     for (int r = 0; r < V; ++r) x[r] = on ? load_as_f32(&p.v[r]) : 0.f;
-    wave_wht(x, d_latent, lane);
+    if constexpr (ROT) wave_wht(x, d_latent, lane);
+    if (norm_lanes > 0) {
+      float ss = 0.f;
+#pragma unroll
+      for (int r = 0; r < V; ++r) ss = fmaf(x[r], x[r], ss);
+      ss = group_reduce<false>(ss, norm_lanes);
+      const float scale = 1.0f / sqrtf(ss * inv_w + eps);
+#pragma unroll
+      for (int r = 0; r < V; ++r) x[r] *= scale;
+    }
 #pragma unroll
     for (int r = 0; r < V; ++r) p.v[r] = store_from_f32<T>(x[r]);
     if (on) reinterpret_cast<Pack<T, V>*>(dst)[lane] = p;
@@ -59,19 +72,23 @@ __global__ __launch_bounds__(kThreads) void append_wht_kernel(T* __restrict__ ca
   }
 }
 
-template <typename T>
-hipError_t launch_wht(T* cache, const T* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
-                      hipStream_t stream) {
+template <typename T, bool ROT>
+hipError_t launch_rows(T* cache, const T* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
+                       int norm_lanes, float eps, hipStream_t stream) {
   // enough waves to keep every CU busy, each then striding over the rows
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>((n + kRowsPerBlock - 1) / kRowsPerBlock, 256 * 16)));
+#define TPLA_ROWS(VV) \
+  hipLaunchKernelGGL((append_row_kernel<T, VV, ROT>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, \
+                     d_rope, norm_lanes, eps)
   switch (d_latent <= 64 ? 1 : d_latent / 64) {
-    case 1: hipLaunchKernelGGL((append_wht_kernel<T, 1>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
-    case 2: hipLaunchKernelGGL((append_wht_kernel<T, 2>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
-    case 4: hipLaunchKernelGGL((append_wht_kernel<T, 4>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
-    case 8: hipLaunchKernelGGL((append_wht_kernel<T, 8>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
-    case 16: hipLaunchKernelGGL((append_wht_kernel<T, 16>), grid, dim3(kThreads), 0, stream, cache, rows, slots, n, d_latent, d_rope); break;
+    case 1: TPLA_ROWS(1); break;
+    case 2: TPLA_ROWS(2); break;
+    case 4: TPLA_ROWS(4); break;
+    case 8: TPLA_ROWS(8); break;
+    case 16: TPLA_ROWS(16); break;
     default: return hipErrorInvalidValue;
   }
+#undef TPLA_ROWS
   return hipGetLastError();
 }
 
@@ -94,24 +111,36 @@ __global__ __launch_bounds__(kThreads) void append_copy_kernel(unsigned char* __
 }  // namespace
 
 hipError_t launch_append(void* cache, const void* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
-                         int dtype, int wht, hipStream_t stream) {
+                         int dtype, int wht, int norm_slices, float eps, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int elem = dtype == 0 ? 4 : 2;
-  if (wht) {
+  if (wht || norm_slices > 0) {
     // a power of two up to 1024 (checked with the descriptor); rows in whole 16-byte pieces
     if (d_latent > kMaxLatent || (d_latent & (d_latent - 1)) != 0 || n > 0x7fffffffLL) return hipErrorInvalidValue;
     if ((d_latent * elem) % 16 != 0 || (d_rope * elem) % 16 != 0) return hipErrorInvalidValue;
-    if (dtype == 0)
-      return launch_wht(static_cast<float*>(cache), static_cast<const float*>(rows), slots, n, d_latent, d_rope, stream);
-    return launch_wht(static_cast<uint16_t*>(cache), static_cast<const uint16_t*>(rows), slots, n, d_latent, d_rope,
-                      stream);
-  } else {
-    const int row_bytes = (d_latent + d_rope) * elem;
-    const int64_t total = n * (row_bytes / 16);
-    const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 256 * 32);
-    hipLaunchKernelGGL(append_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                       static_cast<unsigned char*>(cache), static_cast<const unsigned char*>(rows), slots, n, row_bytes);
+    int norm_lanes = 0;  // lanes holding one normalised slice
+    if (norm_slices > 0) {
+      const int v = d_latent <= 64 ? 1 : d_latent / 64;
+      const int w = d_latent / norm_slices;
+      if (norm_slices > 64 || d_latent % norm_slices != 0 || w % v != 0) return hipErrorInvalidValue;
+      norm_lanes = w / v;
+    }
+    if (dtype == 0) {
+      auto* c = static_cast<float*>(cache);
+      auto* r = static_cast<const float*>(rows);
+      return wht ? launch_rows<float, true>(c, r, slots, n, d_latent, d_rope, norm_lanes, eps, stream)
+                 : launch_rows<float, false>(c, r, slots, n, d_latent, d_rope, norm_lanes, eps, stream);
+    }
+    auto* c = static_cast<uint16_t*>(cache);
+    auto* r = static_cast<const uint16_t*>(rows);
+    return wht ? launch_rows<uint16_t, true>(c, r, slots, n, d_latent, d_rope, norm_lanes, eps, stream)
+               : launch_rows<uint16_t, false>(c, r, slots, n, d_latent, d_rope, norm_lanes, eps, stream);
   }
+  const int row_bytes = (d_latent + d_rope) * elem;
+  const int64_t total = n * (row_bytes / 16);
+  const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 256 * 32);
+  hipLaunchKernelGGL(append_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<unsigned char*>(cache), static_cast<const unsigned char*>(rows), slots, n, row_bytes);
   return hipGetLastError();
 }
 

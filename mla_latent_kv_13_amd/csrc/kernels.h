@@ -79,8 +79,9 @@ int mfma_max_segment_pages();
 // Rotate q_lat [B*H, d_c] by the Hadamard matrix into dst (fp32 if dst_f32, else bf16).
 hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_latent, void* dst, int dst_f32,
                                hipStream_t stream);
+// norm_slices > 0: RMS-normalise the (rotated) latent over that many equal slices, unit gain.
 hipError_t launch_append(void* cache, const void* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
-                         int dtype, int wht, hipStream_t stream);
+                         int dtype, int wht, int norm_slices, float eps, hipStream_t stream);
 // out_v[b,h,:] = W_UV[h] . o[b,h,:]; w_dtype 0 = fp32, 1 = bf16 weights [heads, d_v, d_latent].
 hipError_t launch_up_project(const float* o, const void* w_uv, int w_dtype, int batch, int heads, int d_latent,
                              int d_v, float* out_v, hipStream_t stream);

@@ -49,21 +49,6 @@ struct Vec<1> {
   static __device__ __forceinline__ void fma(float w, const T& v, T& acc) { acc = fmaf(w, v, acc); }
 };
 
-// Maximum (MAX) or sum over aligned groups of gw lanes (gw a power of two <= 64); every lane of a
-// group receives its group's result.  Below 16 lanes: DPP swaps of lane pairs (lane ^ 1, lane ^ 2),
-// then of the two quads of each 8 and the two halves of each 16 (mirrors).
-template <bool MAX>
-__device__ __forceinline__ float group_reduce(float v, int gw) {
-  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
-  if (gw > 1) v = op(v, dpp_mov<0xb1>(v));   // quad_perm(1, 0, 3, 2)
-  if (gw > 2) v = op(v, dpp_mov<0x4e>(v));   // quad_perm(2, 3, 0, 1)
-  if (gw > 4) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
-  if (gw > 8) v = op(v, dpp_mov<0x140>(v));  // row_mirror
-  if (gw > 16) v = op(v, __shfl_xor(v, 16));
-  if (gw > 32) v = op(v, __shfl_xor(v, 32));
-  return v;
-}
-
 // Merge of one (sequence, head) for nb computed shards from s0, in a single pass.  Shard s0 + q's
 // partials are rows q * n2 + k, k < n2 (n2 = a power of two >= the slots per shard nr and >= P;
 // rows k >= nr are padding).  A shard's arithmetic does not depend on s0 or nb.  A

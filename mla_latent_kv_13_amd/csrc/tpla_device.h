@@ -109,6 +109,21 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// Maximum (MAX) or sum over aligned groups of gw lanes (gw a power of two <= 64); every lane of a
+// group receives its group's result.  Below 16 lanes: DPP swaps of lane pairs (lane ^ 1, lane ^ 2),
+// then of the two quads of each 8 and the two halves of each 16 (mirrors).
+template <bool MAX>
+__device__ __forceinline__ float group_reduce(float v, int gw) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if (gw > 1) v = op(v, dpp_mov<0xb1>(v));   // quad_perm(1, 0, 3, 2)
+  if (gw > 2) v = op(v, dpp_mov<0x4e>(v));   // quad_perm(2, 3, 0, 1)
+  if (gw > 4) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
+  if (gw > 8) v = op(v, dpp_mov<0x140>(v));  // row_mirror
+  if (gw > 16) v = op(v, __shfl_xor(v, 16));
+  if (gw > 32) v = op(v, __shfl_xor(v, 32));
+  return v;
+}
+
 // One butterfly of a Walsh-Hadamard stage across lanes: the pair (lane, lane ^ M) becomes
 // (a + c, a - c), a the value of the lane with bit M clear.  The partner's value comes from a
 // VALU lane swap: DPP within rows of 16 (M = 4: the half-row mirror, then the quad reversal,

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("latent_cache_append", "tpla_decode_sharded", "mla_decode_absorbed", "tpla_workspace_size",
-                     "tpla_value_up_projection", "tpla_merge_context_parts"):
+                     "tpla_value_up_projection", "tpla_merge_context_parts", "latent_cache_append_normed"):
         assert required in names
     assert set(names) == set(binding.EXPORTED)
 
@@ -203,3 +203,25 @@ def test_context_merge_validation_before_launch(lib, kw, status):
 
 def test_context_merge_empty_is_a_no_op(lib):
     assert _merge_raw(lib, batch=0, op=0, lp=0, out=0, lse=0)[0] == 0
+
+
+@pytest.mark.parametrize("desc,norm,eps,status", [
+    (DSV3, 0, 1e-6, 1),             # at least one slice
+    (DSV3, 3, 1e-6, 1),             # 3 does not divide 512
+    (DSV3, 2, -1.0, 1),             # negative eps
+    (DSV3, 2, float("inf"), 1),
+    (DSV3, 128, 1e-6, 2),           # more than 64 slices
+    (binding.Desc("bf16", 576, 64, 64, 1000, 1024, "identity"), 1, 1e-6, 2),  # not a power of two
+])
+def test_normed_append_validation(lib, desc, norm, eps, status):
+    cdesc = desc.c()
+    p = ctypes.c_void_p
+    st = lib.latent_cache_append_normed(ctypes.byref(cdesc), p(0x10000), p(0x20000), p(0x30000), 4, norm,
+                                        ctypes.c_float(eps), None)
+    assert st == status, (st, lib.tpla_last_error().decode())
+
+
+def test_normed_append_zero_rows_is_a_no_op(lib):
+    cdesc = DSV3.c()
+    assert lib.latent_cache_append_normed(ctypes.byref(cdesc), None, None, None, 0, 2, ctypes.c_float(1e-6),
+                                          None) == 0
