@@ -196,14 +196,35 @@ def time_workload(w: Workload, steps: int, warmup: int, flush: bool):
     torch.cuda.synchronize()
     call_ms = [e[0].elapsed_time(e[1]) for e in ev]
     dec_ms = [e[0].elapsed_time(e[1]) for e in kev]
+    # the same call captured once in a HIP graph and replayed (how a serving loop would issue it)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        w.call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        w.call()
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evict()
+        gev[i][0].record()
+        graph.replay()
+        gev[i][1].record()
+    torch.cuda.synchronize()
+    graph_ms = [e[0].elapsed_time(e[1]) for e in gev]
+    del graph
     mean_call = statistics.fmean(call_ms)
     mean_dec = statistics.fmean(dec_ms)
     return {
         "call_ms_mean": mean_call, "call_ms_median": statistics.median(call_ms), "call_ms_min": min(call_ms),
         "decode_kernel_ms_mean": mean_dec, "decode_kernel_ms_min": min(dec_ms),
         "tokens_per_s": w.tokens / (mean_call * 1e-3),
+        "query_tokens_per_s": w.case.batch / (mean_call * 1e-3),
         "call_gbs": w.bytes / (mean_call * 1e-3) / 1e9,
         "decode_kernel_gbs": w.bytes / (mean_dec * 1e-3) / 1e9,
+        "graph_replay_ms_mean": statistics.fmean(graph_ms), "graph_replay_ms_median": statistics.median(graph_ms),
         "wall_s_with_flush": wall,
     }
 
@@ -527,6 +548,7 @@ def main():
             w = Workload(cfg, args.chunk_tokens)
             r = time_workload(w, args.extra_steps, args.warmup, not args.no_flush)
             others[w.case.name] = {"config": w.config(), "tokens_per_s": r["tokens_per_s"],
+                                   "query_tokens_per_s": r["query_tokens_per_s"],
                                    "call_ms_mean": r["call_ms_mean"], "hbm_gbs": r["call_gbs"],
                                    "hbm_frac_of_peak": r["call_gbs"] / HBM_PEAK_GBS,
                                    "decode_kernel_gbs": r["decode_kernel_gbs"],

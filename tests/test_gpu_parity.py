@@ -292,3 +292,32 @@ def test_million_token_context_sampled(layout, g, dkw):
         rel, mx = assert_parity(out_np[1, h], ref[0, k], "bf16", f"long {layout} G={g} head {h}")
         _say(f"  head {h}: rel L2 {rel:.2e} max {mx:.2e}")
     assert_lse(lse_np[1][:, LONG_HEADS], ref_lse[0], "bf16", f"long {layout} G={g} long sequence")
+
+
+def test_decode_call_replays_from_a_hip_graph():
+    """A decode call (query rotation, tile-prefix scan, decode kernel, merge) enqueues no memset,
+    allocation or synchronisation, so it can be captured in a HIP graph; every replay, with eager
+    work and synchronisations between replays, equals the eager call bit for bit."""
+    case = inputs.make_case(31, batch=3, heads=64, d_latent=512, d_rope=64, shards=2, lens=[900, 1, 300], paged=True,
+                            page_size=64, transform="wht", scale=1.0 / np.sqrt(192))
+    dc = DeviceCase(case)
+    eager_out, eager_lse = dc.decode()
+    out, lse = torch.empty_like(eager_out), torch.empty_like(eager_lse)
+    ws = binding.alloc_workspace(binding.workspace_size(dc.desc, case.batch, case.heads, 2, 2, case.max_seq_len),
+                                 "cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dc.decode(out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dc.decode(out=out, lse=lse, workspace=ws)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out) and torch.equal(lse, eager_lse)
