@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--chunk-tokens", type=int, default=0)
     p.add_argument("--no-flush", action="store_true", help="do not evict the last-level cache between steps")
+    p.add_argument("--extras-only", action="store_true",
+                   help="only the calls beside the decode: the append (paged Hadamard workload), the value "
+                        "up-projection and the context merge")
     p.add_argument("--calibration-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (to scale HBM byte counters)")
     return p.parse_args()
@@ -509,6 +512,15 @@ def main():
 
     binding.load_library()
     torch.cuda.init()
+    if args.extras_only:
+        w = Workload(5, args.chunk_tokens)
+        extras = {"append": time_append(w, args.extra_steps, args.warmup, not args.no_flush)}
+        del w
+        torch.cuda.empty_cache()
+        extras["value_up_projection"] = time_value_projection(args.extra_steps, args.warmup, not args.no_flush)
+        extras["context_merge"] = time_context_merge(args.extra_steps, args.warmup, not args.no_flush)
+        print(json.dumps(extras), flush=True)
+        return
     head = Workload(args.config, args.chunk_tokens)
     res = time_workload(head, args.steps, args.warmup, not args.no_flush)
     log(f"headline: {json.dumps(res)}")
