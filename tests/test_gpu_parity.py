@@ -44,6 +44,14 @@ SMALL = [
     ("negative_scale", dict(batch=2, heads=64, shards=4, lens=[250, 64], scale=-0.1), {}),
     ("single_tile_and_one_token", dict(batch=3, heads=128, shards=1, lens=[32, 1, 31]), {}),
     ("more_than_64_chunks", dict(batch=2, heads=32, shards=2, lens=[5000, 4100]), dict(chunk_tokens=64)),
+    # eight and sixteen shards: 64- and 32-wide slices (the generic kernel), plain and rotated
+    ("g8_w64_generic", dict(batch=2, heads=16, shards=8, lens=[333, 65]), {}),
+    ("g16_w32_generic_wht", dict(batch=2, heads=8, shards=16, lens=[200, 31], transform="wht", paged=True,
+                                 page_size=16), {}),
+    # 256 heads: two 128-head groups at w = 256, four 64-head groups at w = 512
+    ("g2_h256_two_head_groups", dict(batch=2, heads=256, shards=2, lens=[700, 90]), {}),
+    ("g1_h256_four_head_groups_paged", dict(batch=2, heads=256, shards=1, lens=[400, 129], paged=True,
+                                            page_size=32), {}),
     # Hadamard row widths 256 and 1024 (4 and 16 values per lane) and 32 (fp32, half the lanes idle)
     ("g2_wht_dl256", dict(batch=2, heads=64, d_latent=256, shards=2, lens=[300, 45], transform="wht"), {}),
     ("g4_wht_dl1024_paged", dict(batch=2, heads=32, d_latent=1024, shards=4, lens=[200, 70], transform="wht",
@@ -321,3 +329,18 @@ def test_decode_call_replays_from_a_hip_graph():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager_out) and torch.equal(lse, eager_lse)
+
+
+def test_five_thousand_short_ragged_sequences():
+    """Many short sequences (0..40 tokens, 64-token pages): the tile-prefix scan over 5000 lengths,
+    worker shares crossing hundreds of sequence boundaries, a 5000-row merge grid."""
+    case = inputs.make_case(41, batch=5000, heads=32, d_latent=512, d_rope=64, shards=2, len_range=(0, 40),
+                            paged=True, page_size=64, scale=1.0 / np.sqrt(192))
+    dc = DeviceCase(case)
+    ref, ref_lse = oracle_decode(case)
+    for sched in ("balanced", "chunked"):
+        out, lse = dc.decode(schedule=sched)
+        torch.cuda.synchronize()
+        rel, mx = assert_parity(_np(out), ref, "bf16", f"5000 sequences, {sched}")
+        assert_lse(_np(lse), ref_lse, "bf16", f"5000 sequences, {sched}")
+        _say(f"5000 sequences {sched}: rel L2 {rel:.2e} max {mx:.2e}")
