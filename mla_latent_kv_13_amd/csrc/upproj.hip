@@ -123,12 +123,14 @@ __global__ __launch_bounds__(64 * kSplit) void up_project_mfma_kernel(const floa
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
   load(Set0{}, 0);
-  load(Set1{}, 1);
+  if (nchunks > 1) load(Set1{}, 1);
   for (int c = 0; c < nchunks; c += 2) {
     process(Set0{}, c);
-    load(Set0{}, c + 2);
-    if (c + 1 < nchunks) process(Set1{}, c + 1);
-    load(Set1{}, c + 3);
+    if (c + 2 < nchunks) load(Set0{}, c + 2);
+    if (c + 1 < nchunks) {
+      process(Set1{}, c + 1);
+      if (c + 3 < nchunks) load(Set1{}, c + 3);
+    }
   }
   __syncthreads();  // every wave is done with its staging area
   floatx4_t* part = reinterpret_cast<floatx4_t*>(&o_s[0][0]);  // [kSplit - 1][4][64]
