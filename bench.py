@@ -374,6 +374,80 @@ def time_value_projection(steps: int, warmup: int, flush: bool, batch=32, heads=
             "bound": "hbm"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
+
+
+def time_prefill(steps: int, warmup: int, flush: bool, batch=4, context=4096, new=1024, heads=128):
+    """mla_prefill_absorbed on a chunked-prefill step: `batch` sequences of `context` cached tokens
+    (paged 64-token pages, Hadamard-rotated cache, DeepSeek-V3 widths) whose last `new` tokens are
+    the new prompt tokens, each attending causally to its prefix.  The call is timed with events
+    around it, the split-K kernel alone with the events the library records around it.  Prefill is
+    compute-bound: priced against the dense bf16 matrix peak with 2*H*(2*d_c + d_r) flops per
+    (query row, visible token) pair (logits over [latent | rope] plus the latent-valued output)."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_13_amd import binding, inputs
+
+    dev = "cuda:0"
+    case = inputs.make_case(91, batch=batch, heads=heads, d_latent=512, d_rope=64, shards=1, lens=context,
+                            paged=True, page_size=64, transform="wht", scale=1.0 / np.sqrt(192),
+                            place_rows=False, name=f"prefill-mla-{batch}x{new}-of-{context}-bf16")
+
+    def dev_t(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    desc = binding.Desc(case.dtype, case.d_latent, case.d_rope, case.page_size, case.num_pages,
+                        case.max_pages_per_seq, case.transform)
+    pool = dev_t(case.empty_pool())
+    binding.latent_cache_append(desc, pool, dev_t(case.rows), torch.from_numpy(case.slots).to(dev))
+    qs, q_lat, q_rope = inputs.make_prefill_queries(92, new_tokens=[new] * batch, heads=heads, d_latent=512,
+                                                    d_rope=64)
+    query_start = torch.from_numpy(qs).to(dev)
+    q_lat_t, q_rope_t = dev_t(q_lat), dev_t(q_rope)
+    seq_lens = torch.from_numpy(case.seq_lens).to(dev)
+    block_table = torch.from_numpy(case.block_table).to(dev)
+    nq = int(qs[-1])
+    out = torch.empty((nq, heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((nq, heads), dtype=torch.float32, device=dev)
+    ws = binding.alloc_workspace(binding.prefill_workspace_size(desc, nq, heads, case.max_seq_len), dev)
+
+    def call(events=None):
+        binding.mla_prefill_absorbed(desc, pool, block_table, seq_lens, query_start, q_lat_t, q_rope_t, case.scale,
+                                     case.max_seq_len, out=out, lse=lse, workspace=ws, events=events)
+
+    flush_buf = _flush_buffer() if flush else None
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(2 * steps)]
+    for i in range(2 * steps):
+        if flush_buf is not None:
+            flush_buf.sum()
+        if i < steps:
+            ev[i][0].record()
+            call()
+            ev[i][1].record()
+        else:
+            call(events=(ev[i][0], ev[i][1]))
+    torch.cuda.synchronize()
+    call_ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev[:steps])
+    kern_ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev[steps:])
+    pairs = sum(context - new + j + 1 for j in range(new)) * batch  # (query row, visible token) pairs
+    flops = 2.0 * heads * (2 * 512 + 64) * pairs
+    tflops_call = flops / (call_ms * 1e-3) / 1e12
+    tflops_kernel = flops / (kern_ms * 1e-3) / 1e12
+    del pool, out, lse, ws
+    return {"shape": {"workload": case.name, "sequences": batch, "context": context, "new_tokens_per_sequence": new,
+                      "heads": heads, "d_latent": 512, "d_rope": 64, "layout": "paged", "page_size": 64,
+                      "transform": "wht", "dtype": "bf16"},
+            "call_ms_mean": call_ms, "kernel_ms_mean": kern_ms, "flops": flops,
+            "prompt_tokens_per_s": nq / (call_ms * 1e-3),
+            "tflops_call": tflops_call, "tflops_kernel": tflops_kernel,
+            "roofline": {"bound": "mfma", "achieved": tflops_kernel, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops_kernel / MFMA_BF16_PEAK_TFLOPS}}
+
+
 def time_context_merge(steps: int, warmup: int, flush: bool, parts=4, batch=32, heads=128, d_latent=512):
     """tpla_merge_context_parts timed on its own (events around each call): the results of `parts`
     decode calls over disjoint context parts at the headline shapes (G = 1), against its
@@ -519,6 +593,7 @@ def main():
         torch.cuda.empty_cache()
         extras["value_up_projection"] = time_value_projection(args.extra_steps, args.warmup, not args.no_flush)
         extras["context_merge"] = time_context_merge(args.extra_steps, args.warmup, not args.no_flush)
+        extras["prefill"] = time_prefill(args.extra_steps, args.warmup, not args.no_flush)
         print(json.dumps(extras), flush=True)
         return
     head = Workload(args.config, args.chunk_tokens)
@@ -578,6 +653,8 @@ def main():
     if not args.headline_only:
         line["value_up_projection"] = time_value_projection(args.extra_steps, args.warmup, not args.no_flush)
         line["context_merge"] = time_context_merge(args.extra_steps, args.warmup, not args.no_flush)
+        line["prefill"] = time_prefill(args.extra_steps, args.warmup, not args.no_flush)
+        log(f"prefill: {json.dumps(line['prefill'])}")
         line["achievable_streaming"] = streaming_bandwidth()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_case)

@@ -196,6 +196,61 @@ int32_t mla_decode_absorbed(const tpla_cache_desc_t* desc, const void* cache,
                             float* out, float* lse, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Exact absorbed MLA prefill attention over the latent cache.  Under
+ * prefill/decode separation the prompt keeps exact MLA and only decode is
+ * sliced ([REV] referee report, summary and major comment 2; forward
+ * implications: exact MLA in the compute-bound prefill phase; [ABS] title and
+ * abstract: MLA-style prefilling).  The new tokens' rows must already be in the
+ * cache (latent_cache_append): new token j of sequence b (n_b new tokens, the
+ * last n_b of its seq_lens[b] cached tokens) attends causally to cached tokens
+ * 0 .. seq_lens[b] - n_b + j of its sequence, with the absorbed-decode logit
+ * and value of mla_decode_absorbed:
+ *   out[r] = sum_t softmax_t(scale * (q_latent[r] . C[t] + q_rope[r] . R[t])) C[t]
+ * and lse[r] the log of that softmax's normaliser (natural log), for every
+ * query row r and head.  Under the Hadamard transform the query is rotated and
+ * the output rotated back, as in decode, so out is in the caller's frame.
+ *   cache, block_table, desc: as for tpla_decode_sharded, over the `batch`
+ *               sequences (without a block table sequence b owns page b)
+ *   seq_lens    device, int32 [batch]: cached tokens of sequence b, its new
+ *               tokens included; 0 <= seq_lens[b] <= max_seq_len
+ *   query_start device, int32 [batch + 1], non-decreasing, query_start[0] = 0,
+ *               query_start[batch] = num_queries: the new tokens of sequence b
+ *               are query rows [query_start[b], query_start[b+1]); their count
+ *               n_b must not exceed seq_lens[b]
+ *   num_queries new tokens in the call, 0 .. 65535 (0: nothing is enqueued)
+ *   q_latent    device, [num_queries, heads, d_latent] in desc->dtype
+ *   q_rope      device, [num_queries, heads, d_rope] in desc->dtype
+ *   out         device, fp32 [num_queries, heads, d_latent], fully overwritten
+ *   lse         device, fp32 [num_queries, heads], or NULL
+ *   workspace   device, at least mla_prefill_workspace_size(...) bytes with
+ *               the same num_queries, heads, max_seq_len and opts, 256-byte
+ *               aligned (it holds the row map, split-K partials and, under the
+ *               transform, the rotated query)
+ * Device values are trusted as in decode; a row whose prefix would be empty
+ * (n_b > seq_lens[b]) gives out = 0 and lse = -inf.  Errors, alignment and
+ * shape limits as for mla_decode_absorbed, with num_queries in place of batch.
+ * The rows run through the split-K decode kernels, each over its own prefix,
+ * so the result is the decode of each prefix. */
+int32_t mla_prefill_workspace_size(const tpla_cache_desc_t* desc, int32_t num_queries, int32_t heads,
+                                   int32_t max_seq_len, const tpla_decode_opts_t* opts, size_t* bytes);
+
+int32_t mla_prefill_absorbed(const tpla_cache_desc_t* desc, const void* cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* query_start, int32_t batch, int32_t num_queries,
+                             int32_t heads, int32_t max_seq_len,
+                             const void* q_latent, const void* q_rope, float scale,
+                             float* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* mla_prefill_absorbed with the decode tuning and timing options (opts may be NULL). */
+int32_t mla_prefill_absorbed_ex(const tpla_cache_desc_t* desc, const void* cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* query_start, int32_t batch, int32_t num_queries,
+                                int32_t heads, int32_t max_seq_len,
+                                const void* q_latent, const void* q_rope, float scale,
+                                float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                const tpla_decode_opts_t* opts, void* stream);
+
 /* latent_cache_append with an RMS normalisation of the latent, unit gain ([REV]
  * referee report: Proposition 1, RMSNorm under orthogonal transforms;
  * key_machinery: Condition 1, shard RMS norms proportional to the global norm;

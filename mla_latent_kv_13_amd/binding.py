@@ -27,7 +27,8 @@ SCHEDULES = {"auto": 0, "chunked": 1, "balanced": 2}
 
 EXPORTED = ["tpla_abi_version", "tpla_status_string", "tpla_last_error", "tpla_workspace_size",
             "latent_cache_append", "tpla_decode_sharded", "tpla_decode_sharded_ex", "mla_decode_absorbed",
-            "tpla_value_up_projection", "tpla_merge_context_parts", "latent_cache_append_normed"]
+            "tpla_value_up_projection", "tpla_merge_context_parts", "latent_cache_append_normed",
+            "mla_prefill_workspace_size", "mla_prefill_absorbed", "mla_prefill_absorbed_ex"]
 
 
 class TplaError(RuntimeError):
@@ -103,6 +104,15 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tpla_merge_context_parts.argtypes = [_I32] * 8 + [_P, _P, _P, _P, _P]
     lib.tpla_value_up_projection.restype = _I32
     lib.tpla_value_up_projection.argtypes = [_I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P]
+    lib.mla_prefill_workspace_size.restype = _I32
+    lib.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, ctypes.POINTER(DecodeOpts),
+                                               ctypes.POINTER(ctypes.c_size_t)]
+    prefill_args = [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, ctypes.c_float,
+                    _P, _P, _P, ctypes.c_size_t]
+    lib.mla_prefill_absorbed.restype = _I32
+    lib.mla_prefill_absorbed.argtypes = prefill_args + [_P]
+    lib.mla_prefill_absorbed_ex.restype = _I32
+    lib.mla_prefill_absorbed_ex.argtypes = prefill_args + [ctypes.POINTER(DecodeOpts), _P]
     _LIB = lib
     return lib
 
@@ -237,6 +247,48 @@ def mla_decode_absorbed(desc: Desc, cache: torch.Tensor, block_table: torch.Tens
     _check(lib.mla_decode_absorbed(ctypes.byref(cdesc), _ptr(cache), _ptr(block_table), _ptr(seq_lens), batch, heads,
                                    max_seq_len, _ptr(q_latent), _ptr(q_rope), ctypes.c_float(scale), _ptr(out),
                                    _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def prefill_workspace_size(desc: Desc, num_queries: int, heads: int, max_seq_len: int, chunk_tokens: int = 0,
+                           kernel: str = "auto", schedule: str = "auto") -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    cdesc = desc.c()
+    _check(lib.mla_prefill_workspace_size(ctypes.byref(cdesc), num_queries, heads, max_seq_len,
+                                          _opts(chunk_tokens, kernel, None, schedule), ctypes.byref(out)))
+    return int(out.value)
+
+
+def mla_prefill_absorbed(desc: Desc, cache: torch.Tensor, block_table: torch.Tensor | None, seq_lens: torch.Tensor,
+                         query_start: torch.Tensor, q_latent: torch.Tensor, q_rope: torch.Tensor, scale: float,
+                         max_seq_len: int, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, want_lse: bool = True, chunk_tokens: int = 0,
+                         kernel: str = "auto", events=None, stream=None, schedule: str = "auto"):
+    """Exact absorbed MLA prefill over the cache; returns (out [Nq, H, d_latent], lse [Nq, H] or None).
+
+    ``query_start`` (int32 [batch + 1]) gives each sequence's query rows; the new tokens' rows
+    must already be in the cache (they are the last of seq_lens[b])."""
+    num_queries, heads = int(q_latent.shape[0]), int(q_latent.shape[1])
+    batch = int(query_start.numel()) - 1
+    dev = q_latent.device
+    if seq_lens.dtype != torch.int32 or query_start.dtype != torch.int32 or (
+            block_table is not None and block_table.dtype != torch.int32):
+        raise ValueError("seq_lens, query_start and block_table must be int32")
+    if out is None:
+        out = torch.empty((num_queries, heads, desc.d_latent), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((num_queries, heads), dtype=torch.float32, device=dev)
+    need = prefill_workspace_size(desc, num_queries, heads, max_seq_len, chunk_tokens, kernel, schedule)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    lib = load_library()
+    cdesc = desc.c()
+    _check(lib.mla_prefill_absorbed_ex(ctypes.byref(cdesc), _ptr(cache), _ptr(block_table), _ptr(seq_lens),
+                                       _ptr(query_start), batch, num_queries, heads, max_seq_len, _ptr(q_latent),
+                                       _ptr(q_rope), ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       workspace.numel(), _opts(chunk_tokens, kernel, events, schedule),
+                                       _stream(stream)))
     return out, lse
 
 

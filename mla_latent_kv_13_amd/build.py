@@ -19,7 +19,7 @@ LIB_NAME = "libtpla_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["api.cpp", "decode_generic.hip", "decode_mfma.hip", "merge.hip", "append.hip", "upproj.hip"]
+SOURCES = ["api.cpp", "decode_generic.hip", "decode_mfma.hip", "merge.hip", "append.hip", "upproj.hip", "prefill.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]

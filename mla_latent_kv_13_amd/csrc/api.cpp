@@ -48,7 +48,7 @@ struct Plan {
   int sched;         // 0 chunked, 1 balanced
   int workers;       // balanced: workgroups per (shard, head group)
   int64_t slots;     // partial slots per (shard, head)
-  size_t off_qrot, off_prefix, off_part_o, off_part_lse, total;
+  size_t off_rows, off_qrot, off_prefix, off_part_o, off_part_lse, total;
 };
 
 int32_t check_desc(const tpla_cache_desc_t* d) {
@@ -70,8 +70,10 @@ int32_t check_desc(const tpla_cache_desc_t* d) {
   return TPLA_OK;
 }
 
+// `batch` counts query rows: sequences for a decode call, new tokens for a prefill call
+// (prefill = true), whose row map (prefix length and sequence per row) the workspace also holds.
 int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int32_t num_shards, int32_t shard_count,
-                  int32_t max_seq_len, const tpla_decode_opts_t* opts, Plan* plan) {
+                  int32_t max_seq_len, const tpla_decode_opts_t* opts, Plan* plan, bool prefill = false) {
   int32_t st = check_desc(d);
   if (st != TPLA_OK) return st;
   if (batch < 1 || heads < 1) return fail(TPLA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 1");
@@ -162,6 +164,8 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
   }
 
   size_t off = 0;
+  plan->off_rows = off;
+  if (prefill) off += 2 * round_up(static_cast<size_t>(batch) * 4, 256);
   plan->off_qrot = off;
   if (d->transform == TPLA_LATENT_WHT) {
     const size_t elem = plan->kernel == 1 ? 4 : 2;
@@ -177,14 +181,24 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
   return TPLA_OK;
 }
 
+// Query rows of a prefill call (see mla_prefill_absorbed): query_start [sequences + 1].
+struct PrefillRows {
+  const int32_t* query_start;
+  int32_t sequences;
+};
+
+// One decode call over `batch` query rows.  Decode: row b is sequence b over seq_lens[b] tokens.
+// Prefill (pf non-null): `batch` new-token rows of pf->sequences sequences, each over its causal
+// prefix of the cache (the row map is built on the device first).
 int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t* block_table,
                     const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len, const void* q_latent,
                     const void* q_rope, float scale, int32_t num_shards, int32_t shard_begin, int32_t shard_count,
                     float* out, float* lse, void* workspace, size_t workspace_bytes, const tpla_decode_opts_t* opts,
-                    void* stream_ptr) {
+                    void* stream_ptr, const PrefillRows* pf = nullptr) {
   Plan plan;
-  int32_t st = make_plan(d, batch, heads, num_shards, shard_count, max_seq_len, opts, &plan);
+  int32_t st = make_plan(d, batch, heads, num_shards, shard_count, max_seq_len, opts, &plan, pf != nullptr);
   if (st != TPLA_OK) return st;
+  const int32_t sequences = pf ? pf->sequences : batch;
   if (shard_begin < 0 || shard_begin + shard_count > num_shards)
     return fail(TPLA_ERR_INVALID_ARGUMENT, "shard range [%d, %d) outside [0, %d)", shard_begin, shard_begin + shard_count, num_shards);
   if (!cache || !seq_lens || !q_latent || !out || (d->d_rope > 0 && !q_rope))
@@ -193,7 +207,7 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
     return fail(TPLA_ERR_INVALID_ARGUMENT, "cache, q_latent, q_rope and out must be 16-byte aligned");
   if (!(scale == scale)) return fail(TPLA_ERR_INVALID_ARGUMENT, "scale is NaN");
   if (block_table == nullptr) {
-    if (d->num_pages < batch || d->page_size < max_seq_len)
+    if (d->num_pages < sequences || d->page_size < max_seq_len)
       return fail(TPLA_ERR_INVALID_ARGUMENT, "without a block table sequence b uses page b: need num_pages >= batch and page_size >= max_seq_len");
   } else {
     if (static_cast<int64_t>(d->max_pages_per_seq) * d->page_size < max_seq_len)
@@ -233,8 +247,18 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
   L.sched = plan.sched;
   L.workers = plan.workers;
   L.tile_prefix = reinterpret_cast<const int*>(ws + plan.off_prefix);
+  L.row_seq = nullptr;
 
   hipError_t e;
+  if (pf) {
+    int* row_len = reinterpret_cast<int*>(ws + plan.off_rows);
+    int* row_seq = reinterpret_cast<int*>(ws + plan.off_rows + round_up(static_cast<size_t>(batch) * 4, 256));
+    e = tpla::launch_prefill_rows(pf->query_start, seq_lens, pf->sequences, batch, max_seq_len, row_len, row_seq, stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill row map launch");
+    seq_lens = row_len;  // from here on every row is a decode row over its own prefix
+    L.seq_lens = row_len;
+    L.row_seq = row_seq;
+  }
   if (plan.sched == 1) {
     e = tpla::launch_tile_prefix(seq_lens, batch, reinterpret_cast<int*>(ws + plan.off_prefix), stream);
     if (e != hipSuccess) return hip_fail(e, "tile prefix launch");
@@ -434,6 +458,50 @@ int32_t mla_decode_absorbed(const tpla_cache_desc_t* desc, const void* cache, co
                             void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(desc, cache, block_table, seq_lens, batch, heads, max_seq_len, q_latent, q_rope, scale, 1, 0, 1,
                      out, lse, workspace, workspace_bytes, nullptr, stream);
+}
+
+int32_t mla_prefill_workspace_size(const tpla_cache_desc_t* desc, int32_t num_queries, int32_t heads,
+                                   int32_t max_seq_len, const tpla_decode_opts_t* opts, size_t* bytes) {
+  if (bytes == nullptr) return fail(TPLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (num_queries < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "num_queries must be >= 0");
+  if (num_queries == 0) {
+    const int32_t st = check_desc(desc);
+    if (st != TPLA_OK) return st;
+    *bytes = 0;
+    return ok();
+  }
+  Plan plan;
+  const int32_t st = make_plan(desc, num_queries, heads, 1, 1, max_seq_len, opts, &plan, true);
+  if (st != TPLA_OK) return st;
+  *bytes = plan.total;
+  return ok();
+}
+
+int32_t mla_prefill_absorbed_ex(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* query_start, int32_t batch,
+                                int32_t num_queries, int32_t heads, int32_t max_seq_len, const void* q_latent,
+                                const void* q_rope, float scale, float* out, float* lse, void* workspace,
+                                size_t workspace_bytes, const tpla_decode_opts_t* opts, void* stream) {
+  const int32_t st = check_desc(desc);
+  if (st != TPLA_OK) return st;
+  if (batch < 1 || heads < 1) return fail(TPLA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 1");
+  if (num_queries < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "num_queries must be >= 0");
+  if (query_start == nullptr || seq_lens == nullptr)
+    return fail(TPLA_ERR_INVALID_ARGUMENT, "query_start and seq_lens must not be NULL");
+  if (num_queries == 0) return ok();  // no new tokens: nothing to compute
+  const PrefillRows pf{query_start, batch};
+  return decode_impl(desc, cache, block_table, seq_lens, num_queries, heads, max_seq_len, q_latent, q_rope, scale, 1,
+                     0, 1, out, lse, workspace, workspace_bytes, opts, stream, &pf);
+}
+
+int32_t mla_prefill_absorbed(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* query_start, int32_t batch, int32_t num_queries,
+                             int32_t heads, int32_t max_seq_len, const void* q_latent, const void* q_rope,
+                             float scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return mla_prefill_absorbed_ex(desc, cache, block_table, seq_lens, query_start, batch, num_queries, heads,
+                                 max_seq_len, q_latent, q_rope, scale, out, lse, workspace, workspace_bytes, nullptr,
+                                 stream);
 }
 
 }  // extern "C"

@@ -39,8 +39,9 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeLaunch a
                        : load_as_f32(static_cast<const E*>(a.q_lat) + qrow * d_c + s * w + j);
   }
   for (int j = threadIdx.x; j < d_r; j += kThreads) q[w + j] = load_as_f32(static_cast<const E*>(a.q_rope) + qrow * d_r + j);
+  const int bs = a.row_seq ? a.row_seq[b] : b;  // cache sequence of query row b
   for (int i = threadIdx.x; i < n; i += kThreads)
-    rowoff[i] = cache_row(a.block_table, b, t0 + i, a.page_size, a.max_pages_per_seq) * D;
+    rowoff[i] = cache_row(a.block_table, bs, t0 + i, a.page_size, a.max_pages_per_seq) * D;
   __syncthreads();
 
   float local_max = -INFINITY;

@@ -158,6 +158,7 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     g_next = seg_end;
   }
   const int n_tiles = (t_end - t_begin + kNT - 1) / kNT;
+  const int bs = a.row_seq ? a.row_seq[b] : b;  // cache sequence of query row b
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   const int first_page = LAYOUT ? (page_shift >= 0 ? (t_begin >> page_shift) : t_begin / page_size) : 0;
   if constexpr (LAYOUT != 0) {
     const int last_page = page_shift >= 0 ? ((t_end - 1) >> page_shift) : (t_end - 1) / page_size;
-    const int* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages_per_seq + first_page;
+    const int* bt = a.block_table + static_cast<int64_t>(bs) * a.max_pages_per_seq + first_page;
     for (int i = tid; i <= last_page - first_page; i += C::THREADS) pages[i] = bt[i];
   }
   __syncthreads();
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   auto row_addr = [&](int64_t row) { return cache + row * D * 2; };
   auto row_of = [&](int t) -> int64_t {
     if constexpr (LAYOUT == 0) {
-      return static_cast<int64_t>(b) * page_size + t;
+      return static_cast<int64_t>(bs) * page_size + t;
     } else {
       const int pi = page_shift >= 0 ? (t >> page_shift) : t / page_size;
       const int off = page_shift >= 0 ? (t & (page_size - 1)) : t - pi * page_size;

@@ -34,6 +34,9 @@ struct DecodeLaunch {
   int sched;
   int workers;
   const int* tile_prefix;
+  // Cache sequence of query row b (prefill: several query rows of one sequence, each over its
+  // own causal prefix, seq_lens[b] being the prefix length); null: row b is sequence b.
+  const int* row_seq;
 };
 
 struct MergeLaunch {
@@ -74,6 +77,12 @@ int mfma_max_chunk_pages();
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 // tile_prefix[b] = sum over b' < b of ceil(seq_lens[b'] / 32), b = 0..batch.
 hipError_t launch_tile_prefix(const int* seq_lens, int batch, int* tile_prefix, hipStream_t stream);
+// Query rows of a prefill call: row r in [query_start[b], query_start[b+1]) belongs to sequence
+// b, sits at position seq_lens[b] - n_b + (r - query_start[b]) of its n_b new tokens and sees the
+// cache prefix up to itself: row_len[r] = that position + 1 (clamped to [0, max_seq_len]),
+// row_seq[r] = b.  Rows past query_start[batch] get length 0.
+hipError_t launch_prefill_rows(const int* query_start, const int* seq_lens, int batch, int num_queries,
+                               int max_seq_len, int* row_len, int* row_seq, hipStream_t stream);
 // Largest number of cache pages one segment of the MFMA kernel may span (its LDS page list).
 int mfma_max_segment_pages();
 // Rotate q_lat [B*H, d_c] by the Hadamard matrix into dst (fp32 if dst_f32, else bf16).

@@ -242,3 +242,14 @@ def make_context_parts(seed: int, *, parts: int, batch: int, heads: int, d_laten
     lse = (lse * np.float32(3.0)).astype(np.float32)
     lse[np.random.default_rng([seed, 2]).random(lse.shape) < empty] = -np.inf
     return out, lse
+
+
+def make_prefill_queries(seed: int, *, new_tokens, heads: int, d_latent: int, d_rope: int, dtype: str = "bf16"):
+    """Seeded query rows of a prefill call: sequence b has new_tokens[b] new tokens (the last of
+    its cached rows).  Returns (query_start int32 [B + 1], q_lat [Nq, H, d_c], q_rope [Nq, H, d_r])
+    in ``dtype``; the values are N(0, 1) drawn as float32 and stored like decode queries."""
+    query_start = np.concatenate([[0], np.cumsum(np.asarray(new_tokens, dtype=np.int64))]).astype(np.int32)
+    nq = int(query_start[-1])
+    q_lat = np.random.default_rng([seed, 0]).standard_normal((nq, heads, d_latent), dtype=np.float32)
+    q_rope = np.random.default_rng([seed, 1]).standard_normal((nq, heads, d_rope), dtype=np.float32)
+    return query_start, _to_dtype(q_lat, dtype), _to_dtype(q_rope, dtype)

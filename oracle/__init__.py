@@ -15,6 +15,7 @@ from .tpla_oracle import (  # noqa: F401
     latent_cache_append,
     tpla_decode_sharded,
     mla_decode_absorbed,
+    mla_prefill_absorbed,
     mla_unabsorbed_bruteforce,
     value_up_projection,
     merge_context_parts,

@@ -59,13 +59,9 @@ class DeviceCase:
                                            shard_count=shard_count, **kw)
 
 
-def oracle_decode(case: inputs.Case, seqs=None, shard_begin=0, shard_count=None, heads=None):
-    """Oracle output for sequences `seqs` (all by default) and query heads `heads` (all by
-    default; heads are independent, so a subset is exact) on a compact contiguous pool built
-    from the case's raw rows (the oracle's own append builds rotated caches)."""
-    if seqs is None:
-        seqs = list(range(case.batch))
-    seqs = list(seqs)
+def oracle_pool(case: inputs.Case, seqs):
+    """(pool [len(seqs), T_max, width] float64, lens): a compact contiguous pool of sequences `seqs`
+    built from the case's raw rows (the oracle's own append builds rotated caches)."""
     starts = np.concatenate([[0], np.cumsum(case.seq_lens.astype(np.int64))])
     lens = case.seq_lens[seqs]
     tmax = int(max(1, lens.max()))
@@ -82,6 +78,17 @@ def oracle_decode(case: inputs.Case, seqs=None, shard_begin=0, shard_count=None,
     if case.transform != "identity" and rows:
         pool = oracle.latent_cache_append(pool, np.concatenate(rows), np.concatenate(slots), case.d_latent,
                                           case.transform, case.dtype)
+    return pool, lens
+
+
+def oracle_decode(case: inputs.Case, seqs=None, shard_begin=0, shard_count=None, heads=None):
+    """Oracle output for sequences `seqs` (all by default) and query heads `heads` (all by
+    default; heads are independent, so a subset is exact) on a compact contiguous pool built
+    from the case's raw rows."""
+    if seqs is None:
+        seqs = list(range(case.batch))
+    seqs = list(seqs)
+    pool, lens = oracle_pool(case, seqs)
     q_lat = inputs.stored_to_f64(case.q_lat, case.dtype)[seqs]
     q_rope = inputs.stored_to_f64(case.q_rope, case.dtype)[seqs]
     if heads is not None:

@@ -258,6 +258,129 @@ def pin_p3b_subset_additivity(orc):
         assert _rel(acc, full) <= 1e-13, ("P3b", transform, _rel(acc, full))
 
 
+# ---------------------------------------------------------------- P18 (prefill)
+def pin_p18_prefill_equals_unabsorbed_causal(orc):
+    """Prefill keeps exact MLA over each new token's causal prefix ([REV] referee
+    report, summary: prefill/decode separation): after the value up-projection,
+    every new token's row equals un-absorbed MLA (K and V expanded through W_UK
+    and W_UV by explicit loops) over the cached tokens up to its own position.
+    Sequence 0 continues a cached context (3 new of 7), sequence 1 is a fresh
+    prompt (5 new of 5)."""
+    rng = np.random.default_rng(18)
+    H, d_c, d_r, d_nope, d_v = 2, 8, 4, 3, 5
+    lens, new = (7, 5), (3, 5)
+    scale = 0.41
+    lat = [rng.standard_normal((t, d_c)) for t in lens]
+    rope = [rng.standard_normal((t, d_r)) for t in lens]
+    pool, seq_lens = _pool(lat, rope)
+    query_start = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    nq = int(query_start[-1])
+    q_nope = rng.standard_normal((nq, H, d_nope))
+    q_rope = rng.standard_normal((nq, H, d_r))
+    w_uk = rng.standard_normal((H, d_nope, d_c))
+    w_uv = rng.standard_normal((H, d_v, d_c))
+    q_lat = np.stack([np.stack([w_uk[h].T @ q_nope[r, h] for h in range(H)]) for r in range(nq)])
+    out, lse = orc.mla_prefill_absorbed(pool, None, seq_lens, query_start, q_lat, q_rope, scale)
+    assert out.shape == (nq, H, d_c) and lse.shape == (nq, H)
+    projected = orc.value_up_projection(out, w_uv)
+    for b in range(2):
+        for j in range(new[b]):
+            r = int(query_start[b]) + j
+            vis = lens[b] - new[b] + j + 1
+            ref = orc.mla_unabsorbed_bruteforce(lat[b][:vis], rope[b][:vis], q_nope[r], q_rope[r], w_uk, w_uv, scale)
+            assert _rel(projected[r], ref) <= 1e-12, ("P18", b, j, _rel(projected[r], ref))
+
+
+def _sdpa_causal(pool, seq_lens, query_start, q_lat, q_rope, scale, hmat):
+    """Absorbed prefill through torch's scaled_dot_product_attention (fp64) with
+    an explicit boolean mask: new token j of n sees keys t <= T - n + j."""
+    nq, H, d_c = q_lat.shape
+    out = np.zeros((nq, H, d_c))
+    for b in range(len(seq_lens)):
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        T, n = int(seq_lens[b]), r1 - r0
+        if n == 0:
+            continue
+        c, r = pool[b, :T, :d_c], pool[b, :T, d_c:]
+        qt = q_lat[r0:r1] @ hmat if hmat is not None else q_lat[r0:r1]
+        q = torch.from_numpy(np.ascontiguousarray(np.concatenate([qt, q_rope[r0:r1]], axis=2).transpose(1, 0, 2)))
+        k = torch.from_numpy(np.ascontiguousarray(np.concatenate([c, r], axis=1))).expand(H, T, -1)
+        v = torch.from_numpy(np.ascontiguousarray(c)).expand(H, T, -1)
+        mask = torch.from_numpy(np.arange(T)[None, :] <= (T - n + np.arange(n))[:, None])
+        o = torch.nn.functional.scaled_dot_product_attention(q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0),
+                                                             attn_mask=mask, scale=scale)
+        y = o[0].numpy().transpose(1, 0, 2)
+        out[r0:r1] = y @ hmat if hmat is not None else y
+    return out
+
+
+def pin_p18b_prefill_sdpa_causal(orc):
+    """Prefill = torch SDPA (fp64) with the offset causal mask, on a paged pool,
+    plain and with the Hadamard-rotated cache (scipy's Hadamard matrix); lse of
+    one row against scipy's logsumexp of its visible logits."""
+    rng = np.random.default_rng(181)
+    H, d_c, d_r = 3, 16, 8
+    lens, new = (11, 6, 9), (4, 0, 9)
+    page, B = 4, len(lens)
+    per = (max(lens) + page - 1) // page
+    lat = [rng.standard_normal((t, d_c)) for t in lens]
+    rope = [rng.standard_normal((t, d_r)) for t in lens]
+    pool, seq_lens = _pool(lat, rope, max_len=per * page)
+    query_start = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    nq = int(query_start[-1])
+    q_lat = rng.standard_normal((nq, H, d_c))
+    q_rope = rng.standard_normal((nq, H, d_r))
+    # the same rows in a paged pool of 4-token pages, pages shuffled
+    perm = rng.permutation(B * per)
+    paged = np.full((B * per * page, d_c + d_r), np.nan)
+    bt = np.zeros((B, per), dtype=np.int32)
+    for b in range(B):
+        for i in range(per):
+            bt[b, i] = perm[b * per + i]
+            paged[bt[b, i] * page:(bt[b, i] + 1) * page] = pool[b, i * page:(i + 1) * page]
+    out, lse = orc.mla_prefill_absorbed(paged.reshape(-1, page, d_c + d_r), bt, seq_lens, query_start, q_lat,
+                                        q_rope, 0.3)
+    ref = _sdpa_causal(pool, seq_lens, query_start, q_lat, q_rope, 0.3, None)
+    assert _rel(out, ref) <= 1e-12, ("P18b", _rel(out, ref))
+    r = 2  # sequence 0, new token 2: sees 11 - 4 + 2 + 1 = 10 tokens
+    logits = 0.3 * (q_lat[r] @ pool[0, :10, :d_c].T + q_rope[r] @ pool[0, :10, d_c:].T)
+    assert np.allclose(lse[r], scipy.special.logsumexp(logits, axis=1), rtol=1e-14, atol=1e-13)
+    # rotated cache written by the oracle's own append with exact storage
+    rows = np.concatenate([pool[b, :lens[b]] for b in range(B)])
+    slots = np.concatenate([b * pool.shape[1] + np.arange(lens[b]) for b in range(B)])
+    rot = orc.latent_cache_append(np.full_like(pool, np.nan), rows, slots, d_c, "wht", "f64")
+    out_r, _ = orc.mla_prefill_absorbed(rot, None, seq_lens, query_start, q_lat, q_rope, 0.3, transform="wht")
+    hmat = scipy.linalg.hadamard(d_c).astype(np.float64) / math.sqrt(d_c)
+    rot_ref = pool.copy()
+    rot_ref[:, :, :d_c] = pool[:, :, :d_c] @ hmat
+    ref_r = _sdpa_causal(rot_ref, seq_lens, query_start, q_lat, q_rope, 0.3, hmat)
+    assert _rel(out_r, ref_r) <= 1e-12, ("P18b wht", _rel(out_r, ref_r))
+    assert _rel(out_r, out) <= 1e-12, ("P18b rotation leaves exact MLA unchanged", _rel(out_r, out))
+
+
+def pin_p18c_prefill_closed_forms(orc):
+    """The first token of a fresh prompt sees only itself: its output is its own
+    latent row and its lse its own logit; a sequence without new tokens adds no
+    row; a row with no visible token (more new tokens than cached) is 0 / -inf."""
+    rng = np.random.default_rng(182)
+    H, d_c, d_r = 2, 8, 4
+    lens, new = (5, 3, 2), (5, 0, 3)
+    lat = [rng.standard_normal((t, d_c)) for t in lens]
+    rope = [rng.standard_normal((t, d_r)) for t in lens]
+    pool, seq_lens = _pool(lat, rope)
+    query_start = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    q_lat = rng.standard_normal((8, H, d_c))
+    q_rope = rng.standard_normal((8, H, d_r))
+    out, lse = orc.mla_prefill_absorbed(pool, None, seq_lens, query_start, q_lat, q_rope, 0.5)
+    assert np.array_equal(out[0], np.broadcast_to(lat[0][0], (H, d_c))), out[0]
+    own = 0.5 * (q_lat[0] @ lat[0][0] + q_rope[0] @ rope[0][0])
+    assert np.allclose(lse[0], own, rtol=1e-15, atol=1e-15)
+    # sequence 2: 3 new tokens but 2 cached: row 5 sees nothing, row 6 sees token 0
+    assert np.all(out[5] == 0.0) and np.all(np.isneginf(lse[5]))
+    assert np.array_equal(out[6], np.broadcast_to(lat[2][0], (H, d_c)))
+    assert np.isfinite(lse[7]).all() and not np.array_equal(out[7], out[6])
+
+
 # ---------------------------------------------------------------- P4
 def _sdpa_gla(pool, seq_lens, q_lat, q_rope, scale, G, hmat):
     """TPLA as grouped latent attention with G*H virtual heads through torch's
@@ -584,6 +707,9 @@ ALL_PINS = [
     pin_p8_softmax_lse_scipy,
     pin_p9_value_projection,
     pin_p10_context_split_merge,
+    pin_p18_prefill_equals_unabsorbed_causal,
+    pin_p18b_prefill_sdpa_causal,
+    pin_p18c_prefill_closed_forms,
     pin_paged_gather,
     pin_append,
     pin_p14_rms_norm_in_append,

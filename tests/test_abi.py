@@ -225,3 +225,54 @@ def test_normed_append_zero_rows_is_a_no_op(lib):
     cdesc = DSV3.c()
     assert lib.latent_cache_append_normed(ctypes.byref(cdesc), None, None, None, 0, 2, ctypes.c_float(1e-6),
                                           None) == 0
+
+
+def _prefill_raw(lib, desc, **kw):
+    """Call mla_prefill_absorbed with fake (never dereferenced) device addresses; only for
+    arguments that validation rejects, or that make the call a no-op, before anything is enqueued."""
+    a = dict(cache=0x10000, block_table=0x20000, seq_lens=0x30000, query_start=0x38000, batch=2, num_queries=64,
+             heads=128, max_seq_len=4096, q_latent=0x40000, q_rope=0x50000, scale=0.1, out=0x60000, lse=0,
+             workspace=0x70000, workspace_bytes=1 << 40)
+    a.update(kw)
+    cdesc = desc.c()
+    p = ctypes.c_void_p
+    st = lib.mla_prefill_absorbed(ctypes.byref(cdesc), p(a["cache"]), p(a["block_table"] or None),
+                                  p(a["seq_lens"] or None), p(a["query_start"] or None), a["batch"],
+                                  a["num_queries"], a["heads"], a["max_seq_len"], p(a["q_latent"]), p(a["q_rope"]),
+                                  ctypes.c_float(a["scale"]), p(a["out"]), p(a["lse"] or None), p(a["workspace"]),
+                                  a["workspace_bytes"], None)
+    return st, lib.tpla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(query_start=0), 1),
+    (dict(seq_lens=0), 1),
+    (dict(batch=0), 1),
+    (dict(num_queries=-1), 1),
+    (dict(num_queries=70000), 2),               # more query rows than the merge grid takes
+    (dict(workspace_bytes=16), 3),
+    (dict(out=0x60004), 1),                     # misaligned output
+    (dict(scale=float("nan")), 1),
+    (dict(block_table=0, batch=2000), 1),       # without a block table each sequence owns a page
+])
+def test_prefill_validation_before_launch(lib, kw, status):
+    st, msg = _prefill_raw(lib, DSV3, **kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_prefill_without_new_tokens_is_a_no_op(lib):
+    st, msg = _prefill_raw(lib, DSV3, num_queries=0)
+    assert st == 0 and msg == ""
+    assert binding.prefill_workspace_size(DSV3, 0, 128, 4096) == 0
+
+
+def test_prefill_workspace_holds_the_row_map(lib):
+    # the same rows as a decode call, plus the row map (prefix length and sequence per row)
+    rows = 1000
+    dec = binding.workspace_size(DSV3, rows, 128, 1, 1, 4096)
+    pre = binding.prefill_workspace_size(DSV3, rows, 128, 4096)
+    assert pre == dec + 2 * _ru(rows * 4)
+    contiguous = binding.Desc("bf16", 512, 64, 4096, 8, 0, "identity")
+    assert binding.prefill_workspace_size(contiguous, rows, 128, 4096) == \
+        binding.workspace_size(contiguous, rows, 128, 1, 1, 4096) + 2 * _ru(rows * 4)

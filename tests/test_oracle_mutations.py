@@ -47,6 +47,10 @@ MUTATIONS = {
                              "lat = rows[i, :d_latent]\n        lat = rms_normalize(lat, norm_slices, eps) if norm_slices else lat\n        lat = hmat @ lat if hmat is not None else lat"),
     "norm_eps_outside_root": ("part / np.sqrt(np.mean(part * part, axis=-1, keepdims=True) + eps)",
                               "part / (np.sqrt(np.mean(part * part, axis=-1, keepdims=True)) + eps)"),
+    "prefill_off_by_one": ("visible = length - n_new + j + 1", "visible = length - n_new + j"),
+    "prefill_no_causal_mask": ("visible = length - n_new + j + 1", "visible = length"),
+    "prefill_wrong_query_row": ("r = r0 + j\n", "r = j\n"),
+    "prefill_no_unrotation": ("out[r] = o @ hmat if hmat is not None else o", "out[r] = o"),
     "empty_lse_zero": ("lse = np.full((batch, shard_count, heads), -np.inf, dtype=np.float64)",
                        "lse = np.full((batch, shard_count, heads), 0.0, dtype=np.float64)"),
 }
