@@ -66,6 +66,8 @@ def parse():
     p.add_argument("--extras-only", action="store_true",
                    help="only the calls beside the decode: the append (paged Hadamard workload), the value "
                         "up-projection and the context merge")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="only the absorbed MLA prefill step (4 sequences x 1024 new tokens of 4096 cached)")
     p.add_argument("--calibration-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (to scale HBM byte counters)")
     return p.parse_args()
@@ -586,6 +588,9 @@ def main():
 
     binding.load_library()
     torch.cuda.init()
+    if args.prefill_only:
+        print(json.dumps({"prefill": time_prefill(args.extra_steps, args.warmup, not args.no_flush)}), flush=True)
+        return
     if args.extras_only:
         w = Workload(5, args.chunk_tokens)
         extras = {"append": time_append(w, args.extra_steps, args.warmup, not args.no_flush)}
