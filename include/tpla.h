@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TPLA_ABI_VERSION 2
+#define TPLA_ABI_VERSION 3  /* 3: adds the prefill calls */
 
 typedef enum {
   TPLA_OK = 0,

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert binding.abi_version() == 2
+    assert binding.abi_version() == 3
     assert lib.tpla_status_string(3) == b"TPLA_ERR_WORKSPACE_TOO_SMALL"
 
 
