@@ -545,7 +545,7 @@ def cpu_baseline(c, budget_s: float = 15.0):
     """The fp64 oracle on the host cores, on whole sequences of the headline workload, repeated
     over the batch until about budget_s of work (decode computation only)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     from mla_latent_kv_13_amd import inputs
@@ -567,9 +567,23 @@ def cpu_baseline(c, budget_s: float = 15.0):
         seqs += 1
         b = (b + 1) % c.batch
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    # the same work on one core (BLAS limited to one thread), a shorter sample
+    one_tokens, one_spent, one_seqs = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while one_spent < budget_s / 4:
+            t0 = time.perf_counter()
+            oracle.tpla_decode_sharded(pool[b:b + 1], None if c.block_table is None else c.block_table[b:b + 1],
+                                       c.seq_lens[b:b + 1], q_lat[b:b + 1], q_rope[b:b + 1], c.scale, c.shards,
+                                       transform=c.transform)
+            one_spent += time.perf_counter() - t0
+            one_tokens += int(c.seq_lens[b])
+            one_seqs += 1
+            b = (b + 1) % c.batch
     return {"value": done_tokens / spent, "unit": "cache-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{seqs} whole sequences ({done_tokens} cached tokens) of the {c.name} workload, "
-                      f"fp64 NumPy oracle, {spent:.1f}s; host has {len(os.sched_getaffinity(0))} usable cores"}
+                      f"fp64 NumPy oracle, {spent:.1f}s; host has {len(os.sched_getaffinity(0))} usable cores",
+            "one_core": {"value": one_tokens / one_spent, "unit": "cache-tokens/s", "cores": 1,
+                         "sample": f"{one_seqs} whole sequences ({one_tokens} cached tokens), {one_spent:.1f}s"}}
 
 
 def main():
