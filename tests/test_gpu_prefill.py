@@ -124,3 +124,45 @@ def test_full_size_chunked_prefill_step_sampled():
                                                    float(np.float32(case.scale)), transform="wht")
         assert_parity(got[r:r + 1], ref, "bf16", f"row {r}")
         assert_lse(got_lse[r:r + 1], ref_lse, "bf16", f"row {r}", "wht")
+
+
+def _random_prefill(i):
+    rng = np.random.default_rng([4241, i])
+    dtype = "f32" if rng.random() < 0.15 else "bf16"
+    if dtype == "bf16" and rng.random() < 0.7:  # shapes the matrix-core kernel takes
+        d_latent, d_rope, heads = 512, 64, int(32 * rng.integers(1, 5))
+    else:
+        d_latent, d_rope, heads = int(rng.choice([64, 128, 256])), int(rng.choice([8, 16, 32])), int(rng.integers(1, 9))
+    batch = int(rng.integers(1, 6))
+    lens = [int(x) for x in rng.integers(0, 700, size=batch)]
+    new = []
+    for t in lens:
+        u = rng.random()
+        new.append(t if u < 0.25 else (0 if u < 0.35 else (t + 2 if u < 0.4 else int(rng.integers(0, t + 1)))))
+    paged = bool(rng.random() < 0.6)
+    kw = dict(batch=batch, heads=heads, d_latent=d_latent, d_rope=d_rope, shards=1, lens=lens, dtype=dtype,
+              paged=paged, page_size=int(rng.choice([1, 8, 16, 32, 64])) if paged else 64,
+              transform="wht" if rng.random() < 0.4 else "identity", scale=1.0 / np.sqrt(d_latent + d_rope),
+              extra_pages=1 if paged else 0)
+    schedule = str(rng.choice(["auto", "chunked", "balanced"])) if dtype == "bf16" and d_latent == 512 else "auto"
+    return kw, new, schedule
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_prefill_configuration(i):
+    kw, new, schedule = _random_prefill(i)
+    print(f"prefill config {i}: {kw} new {new} schedule {schedule}", flush=True)
+    case = inputs.make_case(7000 + i, name=f"prefill-random-{i}", **kw)
+    dc = DeviceCase(case)
+    query_start, q_lat, q_rope = _queries(case, 7100 + i, new)
+    if int(query_start[-1]) == 0:
+        return  # no new tokens: the call enqueues nothing (checked in the host tests)
+    out, lse = _prefill(dc, query_start, q_lat, q_rope, schedule=schedule)
+    torch.cuda.synchronize()
+    ref, ref_lse = _oracle(case, query_start, q_lat, q_rope)
+    got = out.cpu().numpy()
+    if np.max(np.abs(ref)) == 0.0:
+        assert np.all(got == 0.0)
+    else:
+        assert_parity(got, ref, case.dtype, f"prefill config {i}")
+    assert_lse(lse.cpu().numpy(), ref_lse, case.dtype, f"prefill config {i}", case.transform)
