@@ -147,15 +147,17 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
   if (req_sched == 2 && !balanced_ok)
     return fail(TPLA_ERR_UNSUPPORTED, "the balanced schedule needs the MFMA kernel and fewer than 2^30 tiles");
   if (balanced_ok && (req_sched == 2 || (req_sched == 0 && d->max_pages_per_seq > 0))) {
-    // One workgroup per slot of the chip, and enough of them that no share of tiles spans more
-    // cache pages than a workgroup stages.
+    // One workgroup per slot of the chip.  A segment (a share's tiles of one sequence) must not
+    // span more cache pages than a workgroup stages; a segment never outgrows its sequence, so
+    // only contexts longer than that bound call for more, shorter shares.
     int head_groups = 1, per_cu = 1;
     tpla::mfma_plan_info(w, heads, &head_groups, &per_cu);
     const int64_t members = static_cast<int64_t>(shard_count) * head_groups;
     int64_t workers = std::max<int64_t>(1, static_cast<int64_t>(kComputeUnits) * per_cu / members);
     if (d->max_pages_per_seq > 0) {
       const int64_t cap_tiles = std::max<int64_t>(1, static_cast<int64_t>(tpla::mfma_max_segment_pages() - 1) * d->page_size / 32 - 1);
-      workers = std::max(workers, (max_tiles + cap_tiles - 1) / cap_tiles);
+      const int64_t span_tiles = (static_cast<int64_t>(span) + 31) / 32;
+      if (span_tiles > cap_tiles) workers = std::max(workers, (max_tiles + cap_tiles - 1) / cap_tiles);
     }
     workers = std::min<int64_t>(workers, std::max<int64_t>(1, max_tiles));
     plan->sched = 1;
