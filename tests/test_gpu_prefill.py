@@ -166,3 +166,29 @@ def test_random_prefill_configuration(i):
     else:
         assert_parity(got, ref, case.dtype, f"prefill config {i}")
     assert_lse(lse.cpu().numpy(), ref_lse, case.dtype, f"prefill config {i}", case.transform)
+
+
+def test_prefill_at_the_row_limit():
+    """The most query rows one call takes (65,535): a single fresh prompt of 65,535 tokens, 32 heads,
+    paged 64-token pages.  Its context is longer than the pages one workgroup stages, so the
+    balanced schedule cuts shares at that bound.  Every output is finite; rows at the tile edges
+    and the far end against the oracle one by one."""
+    n = 65535
+    case = inputs.make_case(95, batch=1, heads=32, d_latent=512, d_rope=64, shards=1, lens=n, paged=True,
+                            page_size=64, scale=1.0 / np.sqrt(192), extra_pages=1, name="prefill-row-limit")
+    dc = DeviceCase(case)
+    query_start, q_lat, q_rope = _queries(case, 96, [n])
+    print("prefill of 65535 new tokens", flush=True)
+    out, lse = _prefill(dc, query_start, q_lat, q_rope)
+    torch.cuda.synchronize()
+    got_lse = lse.cpu().numpy()
+    assert torch.isfinite(out).all().item() and np.all(np.isfinite(got_lse))
+    pool = oracle_pool(case, [0])[0]
+    rng = np.random.default_rng(97)
+    for r in sorted({0, 1, 31, 32, 33, 4095, 32767, n - 2, n - 1, *rng.integers(0, n, size=3).tolist()}):
+        ref, ref_lse = oracle.mla_prefill_absorbed(pool, None, [r + 1], [0, 1],
+                                                   inputs.stored_to_f64(q_lat[r:r + 1], "bf16"),
+                                                   inputs.stored_to_f64(q_rope[r:r + 1], "bf16"),
+                                                   float(np.float32(case.scale)))
+        assert_parity(out[r:r + 1].cpu().numpy(), ref, "bf16", f"row {r}")
+        assert_lse(got_lse[r:r + 1], ref_lse, "bf16", f"row {r}")
