@@ -45,7 +45,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "latent-cache decode tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 # the decode kernel's sources: its file and the LDS-DMA helpers it includes
-KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_13_amd", "csrc", f) for f in ("decode_mfma.hip", "lds_dma.h")]
+KERNEL_SRCS = [os.path.join(ROOT, "mla_latent_kv_13_amd", "csrc", f) for f in ("decode_mfma.hip", "lds_dma.h")] + [
+    os.path.join(ROOT, "mla_latent_kv_13_amd", "build.py")]  # the compiler flags shape the kernel too
 
 
 def log(msg):

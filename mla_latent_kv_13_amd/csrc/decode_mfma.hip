@@ -110,7 +110,11 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   // adjacent in dispatch order, sharing that XCD's L2 for the common rows.
   const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
   const int member = slot % members;
-  const int u = (slot / members) * 8 + xcd;
+  // Prefill rows under the balanced schedule: each XCD takes a contiguous block of workers
+  // instead, so that the rows of one sequence -- which all read the same prefix tiles -- run on
+  // one XCD and share its L2.
+  int u = (slot / members) * 8 + xcd;
+  if (a.row_seq != nullptr && a.sched == 1) u = xcd * ((units + 7) / 8) + slot / members;
   if (u >= units) return;
   const int groups = a.heads / (32 * HB);
   const int s_local = member / groups, hg = member % groups;
