@@ -36,6 +36,7 @@ import os
 import statistics
 import sys
 import time
+import types
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -481,7 +482,8 @@ def time_context_merge(steps: int, warmup: int, flush: bool, parts=4, batch=32, 
     nbytes = (parts + 1) * batch * heads * d_latent * 4 + (parts + 1) * batch * heads * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     del op, lp, out, lse
-    return {"shape": {"parts": parts, "batch": batch, "heads": heads, "d_latent": d_latent, "shards": 1},
+    return {"shape": {"parts": parts, "batch": batch, "heads": heads, "d_latent": d_latent, "shards": 1,
+                      "shard_count": 1, "transform": "identity", "seed": 3, "empty_parts": 0.0},
             "ms_mean": ms, "algorithmic_bytes": nbytes, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
             "bound": "hbm"}
 
@@ -587,6 +589,77 @@ def cpu_baseline(c, budget_s: float = 15.0):
                          "sample": f"{one_seqs} whole sequences ({one_tokens} cached tokens), {one_spent:.1f}s"}}
 
 
+def cpu_baseline_extras(line, append_case=None, budget_s: float = 2.0):
+    """The fp64 oracle timed beside each call the bench times besides the decode (the value
+    up-projection, the context merge, the append and the prefill), each on a bounded sample of
+    the same seeded inputs for about budget_s, scaled to the whole call; set-up (input generation,
+    the rotated cache of the prefill sample) is not timed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from mla_latent_kv_13_amd import inputs
+
+    threads = int(max([d.get("num_threads", 1) for d in threadpool_info()] or [1]))
+
+    def timed(fn, sample, total, unit, what):
+        runs, spent = 0, 0.0
+        while spent < budget_s or runs == 0:
+            t0 = time.perf_counter()
+            fn()
+            spent += time.perf_counter() - t0
+            runs += 1
+        ms = spent / runs * total / sample * 1e3
+        return {"ms_whole_call": ms, "kind": "oracle", "cores": threads,
+                "sample": f"{what}: {sample} of {total} {unit} per run, {runs} runs, {spent:.1f}s, scaled to the whole call"}
+
+    if "value_up_projection" in line:
+        sh = line["value_up_projection"]["shape"]
+        o, w = inputs.make_value_projection(2, batch=sh["batch"], heads=sh["heads"], d_latent=sh["d_latent"], d_v=sh["d_v"])
+        o64, w64 = o.astype(np.float64), inputs.stored_to_f64(w, "bf16")
+        n = sh["batch"] * sh["heads"]
+        line["value_up_projection"]["cpu_baseline"] = timed(lambda: oracle.value_up_projection(o64, w64), n, n,
+                                                            "(sequence, head) rows", "the whole call")
+    if "context_merge" in line:
+        sh = line["context_merge"]["shape"]
+        op, lp = inputs.make_context_parts(sh["seed"], parts=sh["parts"], batch=sh["batch"], heads=sh["heads"],
+                                           d_latent=sh["d_latent"], shard_count=sh["shard_count"], empty=sh["empty_parts"])
+        k = min(4, sh["batch"])
+        line["context_merge"]["cpu_baseline"] = timed(
+            lambda: oracle.merge_context_parts(op[:, :k], lp[:, :k], sh["shards"], 0, sh["shard_count"],
+                                               transform=sh["transform"]), k, sh["batch"], "sequences", "merge")
+    if "append" in line and append_case is not None:
+        c = append_case
+        rows = inputs.stored_to_f64(c.rows, c.dtype)
+        n = rows.shape[0]
+        target = np.full((1, n, c.width), np.nan)
+        line["append"]["cpu_baseline"] = timed(
+            lambda: oracle.latent_cache_append(target, rows, np.arange(n), c.d_latent, c.transform, c.dtype),
+            n, c.total_rows, "rows", f"rotated append of {c.name}")
+    if "prefill" in line:
+        sh = line["prefill"]["shape"]
+        case = inputs.make_case(91, batch=sh["sequences"], heads=sh["heads"], d_latent=sh["d_latent"], d_rope=sh["d_rope"],
+                                shards=1, lens=sh["context"], paged=True, page_size=sh["page_size"],
+                                transform=sh["transform"], scale=1.0 / np.sqrt(192), place_rows=False)
+        qs, q_lat, q_rope = inputs.make_prefill_queries(92, new_tokens=[sh["new_tokens_per_sequence"]] * sh["sequences"],
+                                                        heads=sh["heads"], d_latent=sh["d_latent"], d_rope=sh["d_rope"])
+        T = sh["context"]
+        raw = inputs.stored_to_f64(case.rows[:T], case.dtype)  # sequence 0, rotated once (set-up)
+        pool = oracle.latent_cache_append(np.full((1, T, case.width), np.nan), raw, np.arange(T), case.d_latent,
+                                          case.transform, case.dtype)
+        picks = np.linspace(0, sh["new_tokens_per_sequence"] - 1, 8).astype(int)
+        ql, qr = inputs.stored_to_f64(q_lat[picks], "bf16"), inputs.stored_to_f64(q_rope[picks], "bf16")
+        vis = [T - sh["new_tokens_per_sequence"] + int(j) + 1 for j in picks]
+
+        def rows_sample():
+            for i in range(len(picks)):
+                oracle.mla_prefill_absorbed(pool, None, [vis[i]], [0, 1], ql[i:i + 1], qr[i:i + 1], case.scale,
+                                            transform=case.transform)
+
+        line["prefill"]["cpu_baseline"] = timed(rows_sample, len(picks), int(qs[-1]), "query rows",
+                                                "prefill rows spread over sequence 0's new tokens")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -645,6 +718,7 @@ def main():
         "timing": res,
     }
     head_case = head.case
+    append_case = None
     del head
     torch.cuda.empty_cache()
     if not args.headline_only:
@@ -666,6 +740,10 @@ def main():
                                                                            not args.no_flush)
             if w.case.transform != "identity":
                 line["append"] = time_append(w, args.extra_steps, args.warmup, not args.no_flush)
+                c = w.case
+                append_case = types.SimpleNamespace(rows=c.rows[:2000].copy(), total_rows=int(c.rows.shape[0]),
+                                                    d_latent=c.d_latent, width=c.width, transform=c.transform,
+                                                    dtype=c.dtype, name=c.name)
             log(f"workload {cfg}: {json.dumps(others[w.case.name])}")
             del w
             torch.cuda.empty_cache()
@@ -678,6 +756,8 @@ def main():
         line["achievable_streaming"] = streaming_bandwidth()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(head_case)
+        if not args.headline_only:
+            cpu_baseline_extras(line, append_case=append_case)
     print(json.dumps(line), flush=True)
 
 
