@@ -55,3 +55,16 @@ def test_workload_shapes():
     lens = np.random.default_rng([5, 5]).integers(1024, 65536, size=64, endpoint=True)
     assert int(lens.sum()) == 2085650
     assert sum((int(t) + 63) // 64 for t in lens) == 32624
+
+
+def test_prefill_queries_layout_and_determinism():
+    qs, q_lat, q_rope = inputs.make_prefill_queries(5, new_tokens=[3, 0, 7], heads=4, d_latent=64, d_rope=16)
+    assert qs.dtype == np.int32 and list(qs) == [0, 3, 3, 10]
+    assert q_lat.shape == (10, 4, 64) and q_rope.shape == (10, 4, 16)
+    assert q_lat.dtype == np.uint16 and q_rope.dtype == np.uint16  # bf16 bit patterns
+    again = inputs.make_prefill_queries(5, new_tokens=[3, 0, 7], heads=4, d_latent=64, d_rope=16)
+    assert np.array_equal(again[1], q_lat) and np.array_equal(again[2], q_rope)
+    f32 = inputs.make_prefill_queries(5, new_tokens=[2], heads=1, d_latent=8, d_rope=8, dtype="f32")
+    assert f32[1].dtype == np.float32 and np.isfinite(f32[1]).all()
+    none = inputs.make_prefill_queries(1, new_tokens=[0, 0], heads=2, d_latent=8, d_rope=8)
+    assert list(none[0]) == [0, 0, 0] and none[1].shape == (0, 2, 8)
