@@ -78,7 +78,8 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
   if (st != TPLA_OK) return st;
   if (batch < 1 || heads < 1) return fail(TPLA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 1");
   if (batch > 65535 || static_cast<int64_t>(heads) * shard_count > 65535)
-    return fail(TPLA_ERR_UNSUPPORTED, "batch and heads * shard_count must be <= 65535");
+    return fail(TPLA_ERR_UNSUPPORTED, prefill ? "num_queries and heads must be <= 65535"
+                                              : "batch and heads * shard_count must be <= 65535");
   if (max_seq_len < 0) return fail(TPLA_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0");
   if (num_shards < 1 || d->d_latent % num_shards != 0)
     return fail(TPLA_ERR_INVALID_ARGUMENT, "num_shards=%d must be >= 1 and divide d_latent=%d", num_shards, d->d_latent);

@@ -259,6 +259,8 @@ def test_prefill_validation_before_launch(lib, kw, status):
     st, msg = _prefill_raw(lib, DSV3, **kw)
     assert st == status, (st, msg)
     assert msg
+    if kw.get("num_queries", 0) > 65535:
+        assert "num_queries" in msg, msg
 
 
 def test_prefill_without_new_tokens_is_a_no_op(lib):
