@@ -192,3 +192,39 @@ def test_prefill_at_the_row_limit():
                                                    float(np.float32(case.scale)))
         assert_parity(out[r:r + 1].cpu().numpy(), ref, "bf16", f"row {r}")
         assert_lse(got_lse[r:r + 1], ref_lse, "bf16", f"row {r}")
+
+
+def test_prefill_call_replays_from_a_hip_graph():
+    """A prefill call (row map, tile-prefix scan, query rotation, decode kernel, merge) enqueues no
+    memset, allocation or synchronisation, so it can be captured in a HIP graph; every replay, with
+    eager work and synchronisations between replays, equals the eager call bit for bit."""
+    case = inputs.make_case(33, batch=3, heads=128, d_latent=512, d_rope=64, shards=1, lens=[700, 90, 300],
+                            paged=True, page_size=64, transform="wht", scale=1.0 / np.sqrt(192), extra_pages=1)
+    dc = DeviceCase(case)
+    query_start, q_lat, q_rope = _queries(case, 34, [50, 90, 1])
+    qs_t, ql_t, qr_t = torch.from_numpy(query_start).to(DEV), to_torch(q_lat, "bf16"), to_torch(q_rope, "bf16")
+
+    def call(**kw):
+        return binding.mla_prefill_absorbed(dc.desc, dc.pool, dc.block_table, dc.seq_lens, qs_t, ql_t, qr_t, case.scale,
+                                            case.max_seq_len, **kw)
+
+    eager_out, eager_lse = call()
+    out, lse = torch.empty_like(eager_out), torch.empty_like(eager_lse)
+    ws = binding.alloc_workspace(binding.prefill_workspace_size(dc.desc, int(query_start[-1]), case.heads,
+                                                                case.max_seq_len), DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out=out, lse=lse, workspace=ws)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out) and torch.equal(lse, eager_lse)
