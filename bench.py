@@ -58,7 +58,7 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=30, help="untimed steps first (the first 10-20 calls of a process run ~2%% slow)")
     p.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5], help="headline workload")
     p.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     p.add_argument("--extra-steps", type=int, default=10, help="timed steps of each other workload")
