@@ -278,3 +278,22 @@ def test_prefill_workspace_holds_the_row_map(lib):
     contiguous = binding.Desc("bf16", 512, 64, 4096, 8, 0, "identity")
     assert binding.prefill_workspace_size(contiguous, rows, 128, 4096) == \
         binding.workspace_size(contiguous, rows, 128, 1, 1, 4096) + 2 * _ru(rows * 4)
+
+
+def test_balanced_workers_only_grow_past_the_staged_page_bound(lib):
+    """Balanced schedule (paged cache): one worker per CU slot unless a context is longer than the
+    pages a workgroup stages (1021 pages of 64 rows here, 2041 tiles); workspace sizes show the
+    worker count (partial slots = rows + workers)."""
+    g1 = binding.Desc("bf16", 512, 64, 64, 100_000, 2048, "identity")
+    heads, w = 128, 512  # w = 512: two head groups of 64 per unit, one workgroup per CU -> 128 workers
+
+    def partials(slots):
+        return _ru(slots * heads * w * 4) + _ru(slots * heads * 4)
+
+    # prefill of 4096 rows over contexts of 4096: within the bound, so 128 workers
+    rows = 4096
+    assert binding.prefill_workspace_size(g1, rows, heads, 4096) == 2 * _ru(rows * 4) + _ru((rows + 1) * 4) + \
+        partials(rows + 128)
+    # decode of 64 sequences up to 131072 tokens (4096 tiles > 2041): shares must stay under the bound,
+    # ceil(64 * 4096 / 2041) = 129 workers
+    assert binding.workspace_size(g1, 64, heads, 1, 1, 131072) == _ru(65 * 4) + partials(64 + 129)
