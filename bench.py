@@ -663,9 +663,9 @@ def cpu_baseline_extras(line, append_case=None, budget_s: float = 2.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
-        log("bench.py measures the single-GPU hot path; multi-GPU runs are not part of this build")
+        log("bench.py measures the single-GPU hot path; runs on several GPUs are not supported")
         sys.exit(2)
     if args.calibration_copy:
         calibration_copy()

@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   TPLA_OK = 0,
   TPLA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, bad shard range, misalignment */
-  TPLA_ERR_UNSUPPORTED = 2,        /* a shape or dtype no kernel of this build handles */
+  TPLA_ERR_UNSUPPORTED = 2,        /* a shape or dtype no kernel of this library handles */
   TPLA_ERR_WORKSPACE_TOO_SMALL = 3,
   TPLA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } tpla_status_t;

@@ -203,7 +203,7 @@ def make_case(seed: int, *, batch: int, heads: int, d_latent: int, d_rope: int, 
 
 
 # The five benchmark workloads (synthetic stand-ins with DeepSeek-V3 / Kimi-K2 shapes).
-CONFIGS = {
+WORKLOADS = {
     1: dict(name="tiny-tpla-g2-f32", batch=1, heads=4, d_latent=64, d_rope=16, shards=2, lens=128,
             dtype="f32", scale=1.0 / math.sqrt(48)),
     2: dict(name="dsv3-mla-g1-ctx4k-bf16", batch=32, heads=128, d_latent=512, d_rope=64, shards=1,
@@ -220,7 +220,7 @@ CONFIGS = {
 
 def make_config(cfg: int, *, place_rows: bool | None = None) -> Case:
     """The seeded case for benchmark workload ``cfg`` (1..5); seed = cfg."""
-    kw = dict(CONFIGS[cfg])
+    kw = dict(WORKLOADS[cfg])
     if place_rows is None:
         place_rows = kw.get("transform", "identity") == "identity"
     return make_case(cfg, place_rows=place_rows, **kw)

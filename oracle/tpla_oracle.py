@@ -37,8 +37,7 @@ sequence's cached tokens):
   slicing; the query is rotated the same way so G = 1 is unchanged ([ABS];
   [FR] Directions; [REV] pith_summary).
 
-Readings taken where the pages leave a step open (each also listed in
-DESIGN.md):
+Readings taken where the pages leave a step open:
  A1  slice outputs are summed in latent coordinates: slice s writes columns
      [s*w, (s+1)*w) of a d_c-wide result (the row-parallel output projection
      multiplies slice s by its own rows, so the all-reduce of the projected
