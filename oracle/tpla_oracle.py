@@ -69,6 +69,7 @@ __all__ = [
     "value_up_projection",
     "merge_context_parts",
     "rms_normalize",
+    "mla_prefill_absorbed",
 ]
 
 
@@ -176,13 +177,14 @@ def latent_cache_append(pool, rows, slots, d_latent: int, transform: str, dtype:
     rows = np.asarray(rows, dtype=np.float64)
     if transform not in ("wht", "identity"):
         raise ValueError(f"unknown transform {transform!r}")
-    hmat = hadamard(d_latent) if transform == "wht" else None
-    for i, slot in enumerate(np.asarray(slots).tolist()):
-        lat = hmat @ rows[i, :d_latent] if hmat is not None else rows[i, :d_latent]
-        if norm_slices:
-            lat = rms_normalize(lat, norm_slices, eps)
-        flat[slot, :d_latent] = _store(lat, dtype) if (hmat is not None or norm_slices) else rows[i, :d_latent]
-        flat[slot, d_latent:] = rows[i, d_latent:]
+    # All rows at once: the latent rows of the batch times H (rows are row vectors and H is
+    # symmetric, so x H is H x for each row), then the optional norm per row, then the rounding.
+    lat = rows[:, :d_latent] @ hadamard(d_latent) if transform == "wht" else rows[:, :d_latent]
+    if norm_slices:
+        lat = rms_normalize(lat, norm_slices, eps)
+    slots = np.asarray(slots, dtype=np.int64)
+    flat[slots, :d_latent] = _store(lat, dtype) if (transform == "wht" or norm_slices) else lat
+    flat[slots, d_latent:] = rows[:, d_latent:]
     return flat.reshape(num_pages, page_size, width)
 
 

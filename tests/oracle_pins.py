@@ -384,8 +384,8 @@ def pin_p18c_prefill_closed_forms(orc):
 # ---------------------------------------------------------------- P4
 def _sdpa_gla(pool, seq_lens, q_lat, q_rope, scale, G, hmat):
     """TPLA as grouped latent attention with G*H virtual heads through torch's
-    scaled_dot_product_attention in float64 ([REV] forward implications: the
-    sharding pattern is a GLA special case with doubled heads)."""
+    scaled_dot_product_attention in float64 ([REV] forward implications: TPLA
+    is grouped latent attention over G*H virtual heads, one per (shard, head))."""
     B, H, d_c = q_lat.shape
     w = d_c // G
     out = np.zeros((B, H, d_c))

@@ -31,8 +31,8 @@ MUTATIONS = {
     "gather_wrong_page": ("int(block_table[b][t // page_size])", "int(block_table[b][t % page_size])"),
     "bf16_truncates": ("y = np.rint(x[finite] / quantum) * quantum", "y = np.trunc(x[finite] / quantum) * quantum"),
     "bf16_wrong_precision": ("q_exp = np.maximum(e - 8, -133)", "q_exp = np.maximum(e - 9, -133)"),
-    "append_drops_rope": ("flat[slot, d_latent:] = rows[i, d_latent:]", "flat[slot, d_latent:] = 0.0"),
-    "append_no_rounding": ("flat[slot, :d_latent] = _store(lat, dtype)", "flat[slot, :d_latent] = lat"),
+    "append_drops_rope": ("flat[slots, d_latent:] = rows[:, d_latent:]", "flat[slots, d_latent:] = 0.0"),
+    "append_no_rounding": ("flat[slots, :d_latent] = _store(lat, dtype) if", "flat[slots, :d_latent] = lat if"),
     "shard_output_summed_not_placed": ("y[:, cols] = (p @ c_lat[:, cols]) / z", "y[:, :w] += (p @ c_lat[:, cols]) / z"),
     "rope_from_latent": ("k_rope = rows[:, d_c:]", "k_rope = rows[:, :d_c][:, :rows.shape[1] - d_c]"),
     "projection_transposed_weight": ("out_latent[:, h, :] @ w_uv[h].T", "out_latent[:, h, :] @ w_uv[h][:, ::-1].T"),
@@ -43,8 +43,9 @@ MUTATIONS = {
     "merge_lse_without_max": ("lse[b, i, h] = m + np.log(z)", "lse[b, i, h] = np.log(z)"),
     "norm_sum_not_mean": ("np.mean(part * part, axis=-1, keepdims=True) + eps", "np.sum(part * part, axis=-1, keepdims=True) + eps"),
     "norm_ignores_slices": ("lat = rms_normalize(lat, norm_slices, eps)", "lat = rms_normalize(lat, 1, eps)"),
-    "norm_before_rotation": ("lat = hmat @ rows[i, :d_latent] if hmat is not None else rows[i, :d_latent]",
-                             "lat = rows[i, :d_latent]\n        lat = rms_normalize(lat, norm_slices, eps) if norm_slices else lat\n        lat = hmat @ lat if hmat is not None else lat"),
+    "norm_before_rotation": ("lat = rows[:, :d_latent] @ hadamard(d_latent) if transform == \"wht\" else rows[:, :d_latent]",
+                             "lat = rows[:, :d_latent]\n    lat = rms_normalize(lat, norm_slices, eps) if norm_slices else lat\n"
+                             "    lat = lat @ hadamard(d_latent) if transform == \"wht\" else lat"),
     "norm_eps_outside_root": ("part / np.sqrt(np.mean(part * part, axis=-1, keepdims=True) + eps)",
                               "part / (np.sqrt(np.mean(part * part, axis=-1, keepdims=True)) + eps)"),
     "prefill_off_by_one": ("visible = length - n_new + j + 1", "visible = length - n_new + j"),
