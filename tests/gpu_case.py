@@ -34,16 +34,18 @@ def desc_of(case: inputs.Case) -> binding.Desc:
 
 
 class DeviceCase:
-    """Device copies of a case; the pool is filled by the library's append for rotated caches."""
+    """Device copies of a case.  The pool is filled by the library's append for rotated caches,
+    and also for plain ones when ``via_append`` is set (or the case carries no host pool);
+    otherwise a plain pool is copied from the host."""
 
-    def __init__(self, case: inputs.Case, device=DEV):
+    def __init__(self, case: inputs.Case, device=DEV, via_append: bool = False):
         self.case = case
         self.desc = desc_of(case)
         self.q_lat = to_torch(case.q_lat, case.dtype, device)
         self.q_rope = to_torch(case.q_rope, case.dtype, device)
         self.seq_lens = torch.from_numpy(case.seq_lens).to(device)
         self.block_table = None if case.block_table is None else torch.from_numpy(case.block_table).to(device)
-        if case.transform == "identity" and case.pool is not None:
+        if case.transform == "identity" and case.pool is not None and not via_append:
             self.pool = to_torch(case.pool, case.dtype, device)
         else:
             self.pool = to_torch(case.empty_pool(), case.dtype, device)
@@ -65,11 +67,10 @@ def oracle_pool(case: inputs.Case, seqs):
     starts = np.concatenate([[0], np.cumsum(case.seq_lens.astype(np.int64))])
     lens = case.seq_lens[seqs]
     tmax = int(max(1, lens.max()))
-    raw = inputs.stored_to_f64(case.rows, case.dtype)
     pool = np.full((len(seqs), tmax, case.width), np.nan)
     rows, slots = [], []
     for i, b in enumerate(seqs):
-        r = raw[starts[b]:starts[b + 1]]
+        r = inputs.stored_to_f64(case.rows[starts[b]:starts[b + 1]], case.dtype)
         if case.transform == "identity":
             pool[i, :r.shape[0]] = r
         else:
@@ -95,6 +96,18 @@ def oracle_decode(case: inputs.Case, seqs=None, shard_begin=0, shard_count=None,
         q_lat, q_rope = q_lat[:, list(heads)], q_rope[:, list(heads)]
     return oracle.tpla_decode_sharded(pool, None, lens, q_lat, q_rope, float(np.float32(case.scale)), case.shards,
                                       shard_begin, shard_count, transform=case.transform)
+
+
+def oracle_decode_grouped(case: inputs.Case, seqs=None, group: int = 4, shard_begin=0, shard_count=None):
+    """oracle_decode over `seqs` (all by default), `group` sequences at a time, so that the
+    oracle's fp64 copies of a large cache never exist whole; returns (out, lse) for `seqs`."""
+    seqs = list(range(case.batch)) if seqs is None else list(seqs)
+    outs, lses = [], []
+    for k in range(0, len(seqs), group):
+        o, l = oracle_decode(case, seqs[k:k + group], shard_begin, shard_count)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs), np.concatenate(lses)
 
 
 def parity(got, ref):
