@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -37,9 +38,37 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// MI355X: 256 compute units.  The split-K plan aims at a few workgroups per CU.
-constexpr int kComputeUnits = 256;
 constexpr int kMaxChunksMerge = 4096;
+
+// Compute units and XCDs (accelerator complex dies, each with its own L2) of the current device.
+// The split-K plan sizes its grid to fill every CU once, and the kernels place workgroups that
+// share rows on one XCD.  Read once per device from the runtime, so that a partitioned device (one
+// XCD per partition) or a part with fewer CUs gets a plan of its own shape.  Without a device
+// (e.g. a workspace-size query on a host with no GPU) a whole MI355X is assumed: 256 CUs in 8
+// XCDs.
+constexpr int kMaxDevices = 64;
+struct DeviceShape {
+  int cus, xcds;
+};
+DeviceShape device_shape() {
+  static std::atomic<int> cached[kMaxDevices];  // cus << 8 | xcds, 0 while unknown
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return {256, 8};
+  }
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1 || xcds > 255)
+      xcds = 1;
+    (void)hipGetLastError();
+    v = (std::min(cus, 1 << 22) << 8) | xcds;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return {v >> 8, v & 255};
+}
 
 struct Plan {
   int kernel;        // 1 generic, 2 MFMA
@@ -107,7 +136,7 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
       int head_groups = 1, per_cu = 1;
       tpla::mfma_plan_info(w, heads, &head_groups, &per_cu);
       const int64_t per_index = static_cast<int64_t>(batch) * shard_count * head_groups;
-      const int64_t slots = static_cast<int64_t>(kComputeUnits) * per_cu;
+      const int64_t slots = static_cast<int64_t>(device_shape().cus) * per_cu;
       int64_t per_seq = std::max<int64_t>(1, (slots + per_index - 1) / per_index);
       if (d->max_pages_per_seq > 0) per_seq = std::max<int64_t>(per_seq, 32);  // ragged lengths: finer chunks balance better
       ct = static_cast<int>(round_up((span + per_seq - 1) / per_seq, 64));
@@ -154,7 +183,7 @@ int32_t make_plan(const tpla_cache_desc_t* d, int32_t batch, int32_t heads, int3
     int head_groups = 1, per_cu = 1;
     tpla::mfma_plan_info(w, heads, &head_groups, &per_cu);
     const int64_t members = static_cast<int64_t>(shard_count) * head_groups;
-    int64_t workers = std::max<int64_t>(1, static_cast<int64_t>(kComputeUnits) * per_cu / members);
+    int64_t workers = std::max<int64_t>(1, static_cast<int64_t>(device_shape().cus) * per_cu / members);
     if (d->max_pages_per_seq > 0) {
       const int64_t cap_tiles = std::max<int64_t>(1, static_cast<int64_t>(tpla::mfma_max_segment_pages() - 1) * d->page_size / 32 - 1);
       const int64_t span_tiles = (static_cast<int64_t>(span) + 31) / 32;
@@ -251,6 +280,7 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
   L.workers = plan.workers;
   L.tile_prefix = reinterpret_cast<const int*>(ws + plan.off_prefix);
   L.row_seq = nullptr;
+  L.xcds = device_shape().xcds;
 
   hipError_t e;
   if (pf) {
@@ -432,7 +462,7 @@ int32_t tpla_value_up_projection(int32_t w_dtype, const float* o, const void* w_
     return fail(TPLA_ERR_INVALID_ARGUMENT, "o, w_uv and out_v must be 16-byte aligned");
   if (heads > 65535 || batch > 65535 * 32) return fail(TPLA_ERR_UNSUPPORTED, "heads <= 65535 and batch <= 2097120");
   const hipError_t e = tpla::launch_up_project(o, w_uv, w_dtype, batch, heads, d_latent, d_v, out_v,
-                                               static_cast<hipStream_t>(stream));
+                                               device_shape().xcds, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "up-projection launch");
   return ok();
 }

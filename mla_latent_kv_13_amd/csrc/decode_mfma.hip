@@ -105,16 +105,17 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   constexpr int ST = C::ST;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
 
-  // XCD-aware placement: consecutive workgroups go to the 8 XCDs in turn, so the members of one
-  // unit (its shards and head groups, which read the same tokens) take ids 8 apart: same XCD,
-  // adjacent in dispatch order, sharing that XCD's L2 for the common rows.
-  const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+  // XCD-aware placement: consecutive workgroups go to the device's XCDs in turn, so the members
+  // of one unit (its shards and head groups, which read the same tokens) take ids `xcds` apart:
+  // same XCD, adjacent in dispatch order, sharing that XCD's L2 for the common rows.
+  const int xcds = a.xcds;
+  const int L = blockIdx.x, xcd = L % xcds, slot = L / xcds;
   const int member = slot % members;
   // Prefill rows under the balanced schedule: each XCD takes a contiguous block of workers
   // instead, so that the rows of one sequence -- which all read the same prefix tiles -- run on
   // one XCD and share its L2.
-  int u = (slot / members) * 8 + xcd;
-  if (a.row_seq != nullptr && a.sched == 1) u = xcd * ((units + 7) / 8) + slot / members;
+  int u = (slot / members) * xcds + xcd;
+  if (a.row_seq != nullptr && a.sched == 1) u = xcd * ((units + xcds - 1) / xcds) + slot / members;
   if (u >= units) return;
   const int groups = a.heads / (32 * HB);
   const int s_local = member / groups, hg = member % groups;
@@ -578,7 +579,7 @@ hipError_t launch_one(const DecodeLaunch& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t units = a.sched == 1 ? a.workers : static_cast<int64_t>(a.num_chunks) * a.batch;
   const int members = a.shard_count * (a.heads / (32 * HB));
-  const int64_t blocks = (units + 7) / 8 * 8 * members;
+  const int64_t blocks = (units + a.xcds - 1) / a.xcds * a.xcds * members;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   int page_shift = -1;
   if (LAYOUT != 0 && (a.page_size & (a.page_size - 1)) == 0) page_shift = __builtin_ctz(a.page_size);

@@ -37,6 +37,8 @@ struct DecodeLaunch {
   // Cache sequence of query row b (prefill: several query rows of one sequence, each over its
   // own causal prefix, seq_lens[b] being the prefix length); null: row b is sequence b.
   const int* row_seq;
+  // XCDs of the device: consecutive workgroup ids are dispatched to the XCDs in turn.
+  int xcds;
 };
 
 struct MergeLaunch {
@@ -93,6 +95,6 @@ hipError_t launch_append(void* cache, const void* rows, const int64_t* slots, in
                          int dtype, int wht, int norm_slices, float eps, hipStream_t stream);
 // out_v[b,h,:] = W_UV[h] . o[b,h,:]; w_dtype 0 = fp32, 1 = bf16 weights [heads, d_v, d_latent].
 hipError_t launch_up_project(const float* o, const void* w_uv, int w_dtype, int batch, int heads, int d_latent,
-                             int d_v, float* out_v, hipStream_t stream);
+                             int d_v, float* out_v, int xcds, hipStream_t stream);
 
 }  // namespace tpla

@@ -78,25 +78,6 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
   return r;
 }
 
-// In-place orthonormal Walsh-Hadamard transform of n floats in LDS (n a power of two),
-// Sylvester (natural) order: radix-2 butterflies on pairs (i, i+span) for span = 1, 2, 4, ...,
-// no bit reversal, then a 1/sqrt(n) scale.  Called by all threads of the block.
-__device__ __forceinline__ void block_fwht(float* x, int n) {
-  for (int span = 1; span < n; span <<= 1) {
-    __syncthreads();
-    for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
-      const int i = (p / span) * 2 * span + (p % span);
-      const float a = x[i], c = x[i + span];
-      x[i] = a + c;
-      x[i + span] = a - c;
-    }
-  }
-  __syncthreads();
-  const float norm = 1.0f / sqrtf(static_cast<float>(n));
-  for (int i = threadIdx.x; i < n; i += blockDim.x) x[i] *= norm;
-  __syncthreads();
-}
-
 // V elements of T read or written as one aligned access.
 template <typename T, int V>
 struct alignas(sizeof(T) * V) Pack {

@@ -36,17 +36,18 @@ constexpr int kWStride = kChunk + 8;  // bf16 per staged row of W_UV (16-byte pa
 __global__ __launch_bounds__(64 * kSplit) void up_project_mfma_kernel(const float* __restrict__ o,
                                                                       const uint16_t* __restrict__ w, int batch,
                                                                       int heads, int d_c, int d_v,
-                                                                      float* __restrict__ out) {
+                                                                      float* __restrict__ out, int xcds) {
   __shared__ __attribute__((aligned(16))) float o_s[kSplit][32 * kOStride];  // also the partial tiles, at the end
   __shared__ __attribute__((aligned(16))) uint16_t w_s[kSplit][32 * kWStride];
   static_assert(sizeof(o_s) >= (kSplit - 1) * 4 * 64 * sizeof(floatx4_t), "partial tiles fit the staging area");
   const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
-  // Workgroup id -> (head, batch tile) unit and value tile.  Workgroups are dealt to the 8 XCDs
-  // round-robin by id; the value tiles of one unit all get ids = unit mod 8 (mod 8), so they run on
-  // one XCD and read the unit's rows of o through that XCD's L2 once.  Ids past the last unit exit.
+  // Workgroup id -> (head, batch tile) unit and value tile.  Workgroups are dealt to the device's
+  // XCDs round-robin by id; the value tiles of one unit all get ids = unit (mod xcds), so they run
+  // on one XCD and read the unit's rows of o through that XCD's L2 once.  Ids past the last unit
+  // exit.
   const int vtiles = (d_v + 31) / 32;
-  const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
-  const int unit = (k / vtiles) * 8 + xcd;
+  const int xcd = blockIdx.x % xcds, k = blockIdx.x / xcds;
+  const int unit = (k / vtiles) * xcds + xcd;
   if (unit >= heads * ((batch + 31) / 32)) return;
   const int v0 = (k % vtiles) * 32, h = unit % heads, b0 = (unit / heads) * 32;
   const int half = lane >> 5, l32 = lane & 31;
@@ -181,15 +182,16 @@ __global__ __launch_bounds__(256) void up_project_generic_kernel(const float* __
 }  // namespace
 
 hipError_t launch_up_project(const float* o, const void* w_uv, int w_dtype, int batch, int heads, int d_latent,
-                             int d_v, float* out_v, hipStream_t stream) {
+                             int d_v, float* out_v, int xcds, hipStream_t stream) {
   if (batch == 0 || heads == 0) return hipSuccess;
+  if (xcds < 1) return hipErrorInvalidValue;
   if (w_dtype == 1 && d_latent % 16 == 0) {
     const int64_t units = static_cast<int64_t>(heads) * ((batch + 31) / 32), vt = (d_v + 31) / 32;
-    const int64_t blocks = (units + 7) / 8 * 8 * vt;
+    const int64_t blocks = (units + xcds - 1) / xcds * xcds * vt;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks));
     hipLaunchKernelGGL(up_project_mfma_kernel, grid, dim3(64 * kSplit), 0, stream, o,
-                       static_cast<const uint16_t*>(w_uv), batch, heads, d_latent, d_v, out_v);
+                       static_cast<const uint16_t*>(w_uv), batch, heads, d_latent, d_v, out_v, xcds);
   } else {
     const int64_t total = static_cast<int64_t>(batch) * heads * d_v;
     const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 256 * 64));
