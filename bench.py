@@ -14,17 +14,24 @@ Cache eviction reads a 1 GiB buffer (a reduction with a scalar result): reading 
 clean lines behind, whereas overwriting a buffer would leave up to 256 MB of dirty lines whose
 write-back then competes with the timed kernel's reads.
 
-Prints ONE JSON line.  The headline workload is the DeepSeek-V3-shaped exact MLA
-decode (G = 1, batch 32, 128 heads, latent 512 + rope 64, context 4096, bf16);
-the other workloads (TPLA G = 2 / G = 4 at 32K context, paged + Hadamard with
-ragged contexts) are reported in "workloads" unless --headline-only is given; the
-contiguous TPLA workloads also carry "per_device_share": the call of one shard (what one
-of G devices would read and compute) and the G = 1 call over the same cache.  "append"
-times latent_cache_append on its own on the paged Hadamard workload's rows: the whole
-cache and one row per sequence, rotated and plain (and rotated with a per-shard RMS norm);
-"value_up_projection" times the value
-up-projection that follows the decode (DeepSeek-V3 shapes, bf16 weights); "context_merge" the
-log-sum-exp merge of four decode results over disjoint context parts (headline shapes).
+Prints ONE JSON line.  The headline workload is the paged TPLA decode with the Hadamard
+reparameterisation (G = 2, batch 64, 128 heads, latent 512 + rope 64, 64-token pages with a
+random block table, contexts uniform in [1024, 65536], bf16), the largest configuration of the
+metric that fits one GPU and the one whose contexts reach the 32K regime the pages quote their
+speedups at.  Its "roofline" object prices the split-K decode kernel's time against the HBM peak
+with the algorithmic bytes (every cache element read once), and its "cpu_baseline" times the fp64
+oracle on a bounded sample of the same sequences on the host cores; that leg also reports the
+error of the timed output against the oracle on the sampled sequences.  The other workloads
+(exact MLA at 4K context, TPLA G = 2 and G = 4 at 32K context) are reported in "workloads"
+unless --headline-only is given, each with its own roofline object and oracle sample, and the
+tiny fp32 case as call latency; the contiguous TPLA workloads also carry "per_device_share":
+the call of one shard (what one of G devices would read and compute) and the G = 1 call over the
+same cache.  "append" times latent_cache_append on its own on the paged Hadamard workload's rows:
+the whole cache and one row per sequence, rotated and plain (and rotated with a per-shard RMS
+norm); "value_up_projection" times the value up-projection that follows the decode
+(DeepSeek-V3 shapes, bf16 weights); "context_merge" the log-sum-exp merge of four decode results
+over disjoint context parts (exact MLA shapes at 4K context); "prefill" the absorbed MLA prefill
+of a chunked-prefill step.
 """
 
 from __future__ import annotations
@@ -59,7 +66,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=30, help="untimed steps first (the first 10-20 calls of a process run ~2%% slow)")
-    p.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5], help="headline workload")
+    p.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5], help="headline workload")
+    p.add_argument("--shard-count", type=int, default=0,
+                   help="headline call computes shards [0, n) only (0 = all): n = 1 is one device's share")
     p.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     p.add_argument("--extra-steps", type=int, default=10, help="timed steps of each other workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -92,7 +101,7 @@ def calibration_copy():
 class Workload:
     """Device-resident inputs of one seeded workload plus preallocated outputs and workspace."""
 
-    def __init__(self, cfg: int, chunk_tokens: int = 0):
+    def __init__(self, cfg: int, chunk_tokens: int = 0, shard_count: int = 0):
         import numpy as np
         import torch
 
@@ -125,14 +134,17 @@ class Workload:
             torch.cuda.synchronize()
             del rows, slots
         self.chunk_tokens = chunk_tokens
+        self.shard_count = shard_count if shard_count > 0 else case.shards
         B, H = case.batch, case.heads
         self.out = torch.empty((B, H, case.d_latent), dtype=torch.float32, device=dev)
-        self.lse = torch.empty((B, case.shards, H), dtype=torch.float32, device=dev)
-        need = binding.workspace_size(self.desc, B, H, case.shards, case.shards, case.max_seq_len, chunk_tokens)
+        self.lse = torch.empty((B, self.shard_count, H), dtype=torch.float32, device=dev)
+        need = binding.workspace_size(self.desc, B, H, case.shards, self.shard_count, case.max_seq_len, chunk_tokens)
         self.workspace = binding.alloc_workspace(need, dev)
         self.tokens = case.total_tokens
         elem = 2 if case.dtype == "bf16" else 4
-        self.bytes = self.tokens * (case.d_latent + case.d_rope) * elem
+        # algorithmic bytes: every element of the shards' columns and the rope key read once
+        width = self.shard_count * (case.d_latent // case.shards) + case.d_rope
+        self.bytes = self.tokens * width * elem
         self.binding = binding
         log(f"workload {cfg} ({case.name}): {self.tokens} cached tokens, {self.bytes / 1e6:.1f} MB, "
             f"prepared in {time.time() - t0:.1f}s")
@@ -140,7 +152,8 @@ class Workload:
     def call(self, events=None):
         c = self.case
         self.binding.tpla_decode_sharded(self.desc, self.pool, self.block_table, self.seq_lens, self.q_lat,
-                                         self.q_rope, c.scale, c.shards, c.max_seq_len, out=self.out, lse=self.lse,
+                                         self.q_rope, c.scale, c.shards, c.max_seq_len, shard_begin=0,
+                                         shard_count=self.shard_count, out=self.out, lse=self.lse,
                                          workspace=self.workspace, chunk_tokens=self.chunk_tokens, events=events)
 
     def config(self):
@@ -148,6 +161,8 @@ class Workload:
         d = {"workload": c.name, "batch": c.batch, "heads": c.heads, "d_latent": c.d_latent, "d_rope": c.d_rope,
              "shards": c.shards, "dtype": c.dtype, "transform": c.transform,
              "layout": "paged" if c.paged else "contiguous", "cached_tokens": self.tokens}
+        if self.shard_count != c.shards:
+            d["shards_computed"] = [0, self.shard_count]
         if c.paged:
             d.update(page_size=c.page_size, context="uniform[1024,65536]", max_seq_len=c.max_seq_len)
         else:
@@ -544,49 +559,97 @@ def traffic_for_current_kernel(workload_name: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(c, budget_s: float = 15.0):
-    """The fp64 oracle on the host cores, on whole sequences of the headline workload, repeated
-    over the batch until about budget_s of work (decode computation only)."""
+def roofline_of(w: "Workload", res: dict) -> dict:
+    """Roofline object of the split-K decode kernel of one workload: algorithmic bytes per launch
+    (every cache element of the computed shards' columns and the rope key once) over the kernel's
+    mean time between the events the library records around it, against the HBM peak; traffic =
+    HBM bytes per launch from the committed counter summary when it was taken on this kernel."""
+    gbs = w.bytes / (res["decode_kernel_ms_mean"] * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic_for_current_kernel(w.case.name) if w.shard_count == w.case.shards else None,
+            "kernel": "split-K decode kernel (decode_mfma_kernel)", "algorithmic_bytes_per_launch": w.bytes,
+            "kernel_ms_mean": res["decode_kernel_ms_mean"]}
+
+
+def cpu_baseline(c, gpu_out=None, gpu_lse=None, shard_count=None, budget_s: float = 15.0, one_core_s: float = 0.0):
+    """The fp64 oracle on the host cores, on whole sequences of a workload in a fixed seeded order,
+    until about budget_s of decode computation (and, with one_core_s, the same with BLAS held to
+    one thread, a per-core figure).  Each sequence's oracle cache is built from the raw rows before
+    its timed decode (the rotated cache by the oracle's own append), so only the decode is timed.
+    The oracle's outputs of the sampled sequences are compared with the GPU's timed output:
+    relative L2 and max-abs errors over those sequences, against the bf16 bar of 2e-2 (1e-5 for
+    fp32)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     from mla_latent_kv_13_amd import inputs
 
-    pool = inputs.stored_to_f64(c.pool, c.dtype) if c.pool is not None else None
-    if pool is None:
-        return None
+    shard_count = shard_count or c.shards
+    starts = np.concatenate([[0], np.cumsum(c.seq_lens.astype(np.int64))])
     q_lat = inputs.stored_to_f64(c.q_lat, c.dtype)
     q_rope = inputs.stored_to_f64(c.q_rope, c.dtype)
-    done_tokens, spent, seqs = 0, 0.0, 0
-    b = 0
-    while spent < budget_s:
-        t0 = time.perf_counter()
-        oracle.tpla_decode_sharded(pool[b:b + 1], None if c.block_table is None else c.block_table[b:b + 1],
-                                   c.seq_lens[b:b + 1], q_lat[b:b + 1], q_rope[b:b + 1], c.scale, c.shards,
-                                   transform=c.transform)
-        spent += time.perf_counter() - t0
-        done_tokens += int(c.seq_lens[b])
-        seqs += 1
-        b = (b + 1) % c.batch
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    # the same work on one core (BLAS limited to one thread), a shorter sample
-    one_tokens, one_spent, one_seqs = 0, 0.0, 0
-    with threadpool_limits(limits=1):
-        while one_spent < budget_s / 4:
+    order = [int(b) for b in np.random.default_rng([int(c.meta.get("seed", 0)), 99]).permutation(c.batch)
+             if c.seq_lens[b] > 0]
+    cache, cached_bytes = {}, [0]
+
+    def prepared(b):
+        if b in cache:
+            return cache[b]
+        r = inputs.stored_to_f64(c.rows[starts[b]:starts[b + 1]], c.dtype)
+        pool = np.full((1, r.shape[0], c.width), np.nan)
+        if c.transform == "identity":
+            pool[0] = r
+        else:
+            pool = oracle.latent_cache_append(pool, r, np.arange(r.shape[0]), c.d_latent, c.transform, c.dtype)
+        if cached_bytes[0] + pool.nbytes <= (2 << 30):
+            cache[b] = pool
+            cached_bytes[0] += pool.nbytes
+        return pool
+
+    def run(budget):
+        done, spent, n, k, outs = 0, 0.0, 0, 0, {}
+        while spent < budget or n == 0:
+            b = order[k % len(order)]
+            pool = prepared(b)
             t0 = time.perf_counter()
-            oracle.tpla_decode_sharded(pool[b:b + 1], None if c.block_table is None else c.block_table[b:b + 1],
-                                       c.seq_lens[b:b + 1], q_lat[b:b + 1], q_rope[b:b + 1], c.scale, c.shards,
-                                       transform=c.transform)
-            one_spent += time.perf_counter() - t0
-            one_tokens += int(c.seq_lens[b])
-            one_seqs += 1
-            b = (b + 1) % c.batch
-    return {"value": done_tokens / spent, "unit": "cache-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{seqs} whole sequences ({done_tokens} cached tokens) of the {c.name} workload, "
-                      f"fp64 NumPy oracle, {spent:.1f}s; host has {len(os.sched_getaffinity(0))} usable cores",
-            "one_core": {"value": one_tokens / one_spent, "unit": "cache-tokens/s", "cores": 1,
-                         "sample": f"{one_seqs} whole sequences ({one_tokens} cached tokens), {one_spent:.1f}s"}}
+            o, l = oracle.tpla_decode_sharded(pool, None, c.seq_lens[b:b + 1], q_lat[b:b + 1], q_rope[b:b + 1],
+                                              float(np.float32(c.scale)), c.shards, 0, shard_count,
+                                              transform=c.transform)
+            spent += time.perf_counter() - t0
+            done += int(c.seq_lens[b])
+            n += 1
+            k += 1
+            outs.setdefault(b, (o[0], l[0]))
+        return done, spent, n, outs
+
+    done, spent, n, outs = run(budget_s)
+    threads = int(max([d.get("num_threads", 1) for d in threadpool_info()] or [1]))
+    res = {"value": done / spent, "unit": "cache-tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} whole-sequence decodes ({done} cached tokens, {len(outs)} distinct sequences) of the "
+                     f"{c.name} workload, fp64 NumPy oracle, {spent:.1f}s of decode; oracle caches built from the "
+                     f"raw rows outside the timing; host has {len(os.sched_getaffinity(0))} usable cores"}
+    if one_core_s > 0:
+        with threadpool_limits(limits=1):
+            d1, s1, n1, _ = run(one_core_s)
+        res["one_core"] = {"value": d1 / s1, "unit": "cache-tokens/s", "cores": 1,
+                           "sample": f"{n1} whole-sequence decodes ({d1} cached tokens), {s1:.1f}s"}
+    if gpu_out is not None:
+        seqs = sorted(outs)
+        ref = np.stack([outs[b][0] for b in seqs])
+        ref_lse = np.stack([outs[b][1] for b in seqs])
+        got = np.asarray(gpu_out, dtype=np.float64)[seqs]
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        mx = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        tol = 2e-2 if c.dtype == "bf16" else 1e-5
+        par = {"sequences": seqs, "rel_l2": rel, "max_abs_over_max_ref": mx, "tolerance": tol,
+               "pass": bool(np.all(np.isfinite(got)) and rel <= tol and mx <= tol)}
+        if gpu_lse is not None:
+            gl = np.asarray(gpu_lse, dtype=np.float64)[seqs]
+            fin = np.isfinite(ref_lse)
+            par["lse_max_err_rel"] = float(np.max(np.abs(gl[fin] - ref_lse[fin]) / np.maximum(1.0, np.abs(ref_lse[fin]))))
+        res["parity_of_timed_output"] = par
+    return res
 
 
 def cpu_baseline_extras(line, append_case=None, budget_s: float = 2.0):
@@ -689,11 +752,9 @@ def main():
         extras["prefill"] = time_prefill(args.extra_steps, args.warmup, not args.no_flush)
         print(json.dumps(extras), flush=True)
         return
-    head = Workload(args.config, args.chunk_tokens)
+    head = Workload(args.config, args.chunk_tokens, args.shard_count)
     res = time_workload(head, args.steps, args.warmup, not args.no_flush)
     log(f"headline: {json.dumps(res)}")
-    traffic = traffic_for_current_kernel(head.case.name)
-    dec_gbs = res["decode_kernel_gbs"]
     line = {
         "metric": METRIC,
         "value": res["tokens_per_s"],
@@ -710,44 +771,58 @@ def main():
         "config": head.config(),
         "hbm_gbs": res["call_gbs"],
         "hbm_frac_of_peak": res["call_gbs"] / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "split-K decode kernel (decode_mfma_kernel)",
-                     "algorithmic_bytes_per_launch": head.bytes,
-                     "kernel_ms_mean": res["decode_kernel_ms_mean"]},
+        "roofline": roofline_of(head, res),
         "timing": res,
     }
-    head_case = head.case
+    head_case, head_shards = head.case, head.shard_count
+    head_out, head_lse = head.out.cpu().numpy(), head.lse.cpu().numpy()
     append_case = None
     del head
     torch.cuda.empty_cache()
+    extra_cpu = {}
     if not args.headline_only:
         others = {}
-        for cfg in (2, 3, 4, 5):
+        for cfg in (1, 2, 3, 4, 5):
             if cfg == args.config:
                 continue
             w = Workload(cfg, args.chunk_tokens)
-            r = time_workload(w, args.extra_steps, args.warmup, not args.no_flush)
-            others[w.case.name] = {"config": w.config(), "tokens_per_s": r["tokens_per_s"],
-                                   "query_tokens_per_s": r["query_tokens_per_s"],
-                                   "call_ms_mean": r["call_ms_mean"], "hbm_gbs": r["call_gbs"],
-                                   "hbm_frac_of_peak": r["call_gbs"] / HBM_PEAK_GBS,
-                                   "decode_kernel_gbs": r["decode_kernel_gbs"],
-                                   "decode_kernel_frac_of_peak": r["decode_kernel_gbs"] / HBM_PEAK_GBS,
-                                   "traffic": traffic_for_current_kernel(w.case.name)}
-            if w.case.shards > 1 and not w.case.paged:
+            if cfg == 1:
+                # launch-bound: call latency, no cache eviction (the whole cache is 40 KB)
+                r = time_workload(w, args.extra_steps * 3, args.warmup, False)
+                others[w.case.name] = {"config": w.config(), "call_us_mean": r["call_ms_mean"] * 1e3,
+                                       "call_us_median": r["call_ms_median"] * 1e3, "call_us_min": r["call_ms_min"] * 1e3,
+                                       "graph_replay_us_median": r["graph_replay_ms_median"] * 1e3,
+                                       "what": "latency of one call (tiny fp32 TPLA decode), launch-bound"}
+            else:
+                r = time_workload(w, args.extra_steps, args.warmup, not args.no_flush)
+                others[w.case.name] = {"config": w.config(), "tokens_per_s": r["tokens_per_s"],
+                                       "query_tokens_per_s": r["query_tokens_per_s"],
+                                       "call_ms_mean": r["call_ms_mean"], "hbm_gbs": r["call_gbs"],
+                                       "hbm_frac_of_peak": r["call_gbs"] / HBM_PEAK_GBS,
+                                       "roofline": roofline_of(w, r)}
+            extra_cpu[w.case.name] = (w.case, w.out.cpu().numpy(), w.lse.cpu().numpy())
+            if w.case.shards > 1 and not w.case.paged and cfg != 1:
                 others[w.case.name]["per_device_share"] = time_shard_calls(w, args.extra_steps, args.warmup,
                                                                            not args.no_flush)
-            if w.case.transform != "identity":
+            if w.case.transform != "identity" and w.case.paged:
                 line["append"] = time_append(w, args.extra_steps, args.warmup, not args.no_flush)
-                c = w.case
-                append_case = types.SimpleNamespace(rows=c.rows[:2000].copy(), total_rows=int(c.rows.shape[0]),
-                                                    d_latent=c.d_latent, width=c.width, transform=c.transform,
-                                                    dtype=c.dtype, name=c.name)
             log(f"workload {cfg}: {json.dumps(others[w.case.name])}")
             del w
             torch.cuda.empty_cache()
         line["workloads"] = others
+    if not args.headline_only and "append" not in line and head_case.transform != "identity":
+        w = Workload(args.config, args.chunk_tokens)
+        line["append"] = time_append(w, args.extra_steps, args.warmup, not args.no_flush)
+        del w
+        torch.cuda.empty_cache()
+    if "append" in line:
+        # the oracle's append is timed on a sample of the rows the append was timed on
+        src = head_case if (head_case.paged and head_case.transform != "identity") else next(
+            (cc for cc, _, _ in extra_cpu.values() if cc.paged and cc.transform != "identity"), None)
+        if src is not None:
+            append_case = types.SimpleNamespace(rows=src.rows[:2000].copy(), total_rows=int(src.rows.shape[0]),
+                                                d_latent=src.d_latent, width=src.width, transform=src.transform,
+                                                dtype=src.dtype, name=src.name)
     if not args.headline_only:
         line["value_up_projection"] = time_value_projection(args.extra_steps, args.warmup, not args.no_flush)
         line["context_merge"] = time_context_merge(args.extra_steps, args.warmup, not args.no_flush)
@@ -755,7 +830,10 @@ def main():
         log(f"prefill: {json.dumps(line['prefill'])}")
         line["achievable_streaming"] = streaming_bandwidth()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(head_case)
+        line["cpu_baseline"] = cpu_baseline(head_case, head_out, head_lse, head_shards, budget_s=10.0, one_core_s=2.0)
+        log(f"cpu_baseline: {json.dumps(line['cpu_baseline'])}")
+        for name, (c, out, lse) in extra_cpu.items():
+            line["workloads"][name]["cpu_baseline"] = cpu_baseline(c, out, lse, budget_s=1.0 if c.batch == 1 else 3.0)
         if not args.headline_only:
             cpu_baseline_extras(line, append_case=append_case)
     print(json.dumps(line), flush=True)
