@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TPLA_ABI_VERSION 3  /* 3: adds the prefill calls */
+#define TPLA_ABI_VERSION 4  /* 3: adds the prefill calls; 4: the allocation-free decode */
 
 typedef enum {
   TPLA_OK = 0,
@@ -183,6 +183,30 @@ int32_t tpla_decode_sharded_ex(const tpla_cache_desc_t* desc, const void* cache,
                                int32_t num_shards, int32_t shard_begin, int32_t shard_count,
                                float* out, float* lse, void* workspace, size_t workspace_bytes,
                                const tpla_decode_opts_t* opts, void* stream);
+
+/* tpla_decode_sharded for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results, without the
+ * workspace arguments.  The scratch the call needs (split-K partials, the tile
+ * prefix, the rotated query) lives in one static device array of 64 MiB
+ * (67,108,864 bytes) inside the library, which each GPU the library runs on
+ * holds until the process ends; its device address is looked up once per
+ * device on the first call there.  The call allocates nothing and frees
+ * nothing.  A call whose scratch need (tpla_workspace_size with opts = NULL)
+ * exceeds 64 MiB returns TPLA_ERR_WORKSPACE_TOO_SMALL and enqueues nothing.
+ * Every call on one GPU shares that GPU's array and the array keeps the last
+ * call's contents (nothing in it needs to start cleared): calls that overlap
+ * on one GPU -- on different streams, or from different threads -- race and
+ * give undefined results; serialise them (one stream) or use
+ * tpla_decode_sharded with a workspace per stream.  Errors as for
+ * tpla_decode_sharded, plus TPLA_ERR_HIP when the scratch address cannot be
+ * looked up. */
+int32_t tpla_decode_sharded_noalloc(const tpla_cache_desc_t* desc, const void* cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int32_t batch, int32_t heads, int32_t max_seq_len,
+                                    const void* q_latent, const void* q_rope, float scale,
+                                    int32_t num_shards, int32_t shard_begin, int32_t shard_count,
+                                    float* out, float* lse, void* stream);
 
 /* Exact weight-absorbed MLA decode ([REV] referee report, significance:
  * matrix absorption; [FR] Tests / validation: G = 1 must equal head-parallel

@@ -28,7 +28,8 @@ SCHEDULES = {"auto": 0, "chunked": 1, "balanced": 2}
 EXPORTED = ["tpla_abi_version", "tpla_status_string", "tpla_last_error", "tpla_workspace_size",
             "latent_cache_append", "tpla_decode_sharded", "tpla_decode_sharded_ex", "mla_decode_absorbed",
             "tpla_value_up_projection", "tpla_merge_context_parts", "latent_cache_append_normed",
-            "mla_prefill_workspace_size", "mla_prefill_absorbed", "mla_prefill_absorbed_ex"]
+            "mla_prefill_workspace_size", "mla_prefill_absorbed", "mla_prefill_absorbed_ex",
+            "tpla_decode_sharded_noalloc"]
 
 
 class TplaError(RuntimeError):
@@ -94,6 +95,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tpla_decode_sharded.argtypes = decode_args + [_P]
     lib.tpla_decode_sharded_ex.restype = _I32
     lib.tpla_decode_sharded_ex.argtypes = decode_args + [ctypes.POINTER(DecodeOpts), _P]
+    lib.tpla_decode_sharded_noalloc.restype = _I32
+    lib.tpla_decode_sharded_noalloc.argtypes = decode_args[:-2] + [_P]
     lib.mla_decode_absorbed.restype = _I32
     lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
@@ -225,6 +228,25 @@ def tpla_decode_sharded(desc: Desc, cache: torch.Tensor, block_table: torch.Tens
                                       max_seq_len, _ptr(q_latent), _ptr(q_rope), ctypes.c_float(scale), num_shards,
                                       shard_begin, shard_count, _ptr(out), _ptr(lse), _ptr(workspace),
                                       workspace.numel(), _opts(chunk_tokens, kernel, events, schedule), _stream(stream)))
+    return out, lse
+
+
+def tpla_decode_sharded_noalloc(desc: Desc, cache: torch.Tensor, block_table: torch.Tensor | None,
+                                seq_lens: torch.Tensor, q_latent: torch.Tensor, q_rope: torch.Tensor, scale: float,
+                                num_shards: int, max_seq_len: int, out: torch.Tensor, lse: torch.Tensor | None,
+                                shard_begin: int = 0, shard_count: int | None = None, stream=None):
+    """TPLA decode through the allocation-free entry point (the library's static scratch); the
+    caller passes the outputs, nothing is allocated.  Returns (out, lse)."""
+    if shard_count is None:
+        shard_count = num_shards - shard_begin
+    batch, heads = int(q_latent.shape[0]), int(q_latent.shape[1])
+    if seq_lens.dtype != torch.int32 or (block_table is not None and block_table.dtype != torch.int32):
+        raise ValueError("seq_lens and block_table must be int32")
+    lib = load_library()
+    cdesc = desc.c()
+    _check(lib.tpla_decode_sharded_noalloc(ctypes.byref(cdesc), _ptr(cache), _ptr(block_table), _ptr(seq_lens), batch,
+                                           heads, max_seq_len, _ptr(q_latent), _ptr(q_rope), ctypes.c_float(scale),
+                                           num_shards, shard_begin, shard_count, _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

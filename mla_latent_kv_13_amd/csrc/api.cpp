@@ -70,6 +70,31 @@ DeviceShape device_shape() {
   return {v >> 8, v & 255};
 }
 
+// Scratch of the allocation-free decode entry point (tpla_decode_sharded_noalloc): one
+// file-scope device array, which every GPU the library runs on holds from the module's load until
+// the process ends.  Host code never passes `scratch` itself (in host code the name is a host-side
+// stand-in, not a device address): the device address is read once per device with
+// hipGetSymbolAddress, with that device current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int32_t scratch_address(void** ptr) {
+  static std::atomic<void*> per_device[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TPLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TPLA_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev, kMaxDevices);
+  void* p = per_device[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(TPLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    per_device[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return TPLA_OK;
+}
+
 struct Plan {
   int kernel;        // 1 generic, 2 MFMA
   int chunk_tokens;
@@ -483,6 +508,26 @@ int32_t tpla_decode_sharded_ex(const tpla_cache_desc_t* desc, const void* cache,
                                size_t workspace_bytes, const tpla_decode_opts_t* opts, void* stream) {
   return decode_impl(desc, cache, block_table, seq_lens, batch, heads, max_seq_len, q_latent, q_rope, scale, num_shards,
                      shard_begin, shard_count, out, lse, workspace, workspace_bytes, opts, stream);
+}
+
+int32_t tpla_decode_sharded_noalloc(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
+                                    const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len,
+                                    const void* q_latent, const void* q_rope, float scale, int32_t num_shards,
+                                    int32_t shard_begin, int32_t shard_count, float* out, float* lse, void* stream) {
+  // The plan (and with it the scratch this call needs) is the one tpla_decode_sharded makes; the
+  // kernels write every scratch byte they later read, so nothing is cleared between calls.
+  Plan plan;
+  const int32_t st = make_plan(desc, batch, heads, num_shards, shard_count, max_seq_len, nullptr, &plan);
+  if (st != TPLA_OK) return st;
+  if (plan.total > kScratchBytes)
+    return fail(TPLA_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                "(use tpla_decode_sharded with a caller workspace)", plan.total, kScratchBytes);
+  void* ws = nullptr;
+  const int32_t sst = scratch_address(&ws);
+  if (sst != TPLA_OK) return sst;
+  return decode_impl(desc, cache, block_table, seq_lens, batch, heads, max_seq_len, q_latent, q_rope, scale, num_shards,
+                     shard_begin, shard_count, out, lse, ws, kScratchBytes, nullptr, stream);
 }
 
 int32_t mla_decode_absorbed(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
