@@ -29,7 +29,8 @@ the call of one shard (what one of G devices would read and compute) and the G =
 same cache.  "append" times latent_cache_append on its own on the paged Hadamard workload's rows:
 the whole cache and one row per sequence, rotated and plain (and rotated with a per-shard RMS
 norm); "value_up_projection" times the value up-projection that follows the decode
-(DeepSeek-V3 shapes, bf16 weights); "context_merge" the log-sum-exp merge of four decode results
+(DeepSeek-V3 shapes, bf16 weights); "projected_decode" (headline workload, and the 4K MLA one)
+the decode with that projection fused into its merge against the two calls; "context_merge" the log-sum-exp merge of four decode results
 over disjoint context parts (exact MLA shapes at 4K context); "prefill" the absorbed MLA prefill
 of a chunked-prefill step.
 """
@@ -391,6 +392,79 @@ def time_value_projection(steps: int, warmup: int, flush: bool, batch=32, heads=
     return {"shape": {"batch": batch, "heads": heads, "d_latent": d_latent, "d_v": d_v, "weights": "bf16"},
             "ms_mean": ms, "algorithmic_bytes": nbytes, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
             "bound": "hbm"}
+
+
+def time_projected(w: Workload, steps: int, warmup: int, flush: bool, d_v: int = 128):
+    """tpla_decode_sharded_projected -- the decode with the value up-projection fused into its
+    merge, writing [B, H, d_v] -- against the unfused pair (tpla_decode_sharded, then
+    tpla_value_up_projection) on the same workload with seeded bf16 weights of DeepSeek-V3's value
+    width.  The two alternate step by step (the decode kernel's own time drifts with the card's
+    clock over a run, and alternating exposes both to the same drift).  Each step is timed with
+    events around the whole call; a second set of steps times what follows the split-K decode
+    kernel (from the event the library records at its end to the end of the call: the fused merge,
+    or the merge and the up-projection), the part the fusion changes.  Algorithmic bytes of the
+    fused call: the cache once, the weights once and the projected output once."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_13_amd import inputs
+
+    c, binding = w.case, w.binding
+    B, H = c.batch, c.heads
+    _, wuv = inputs.make_value_projection(40 + w.cfg, batch=1, heads=H, d_latent=c.d_latent, d_v=d_v)
+    w_t = torch.from_numpy(wuv.view("int16")).view(torch.bfloat16).to("cuda:0")
+    out_f = torch.empty((B, H, d_v), dtype=torch.float32, device="cuda:0")
+    out_p = torch.empty_like(out_f)
+    flush_buf = _flush_buffer() if flush else None
+
+    def fused(events=None):
+        binding.tpla_decode_sharded_projected(w.desc, w.pool, w.block_table, w.seq_lens, w.q_lat, w.q_rope, c.scale,
+                                              c.shards, c.max_seq_len, w_t, shard_begin=0,
+                                              shard_count=w.shard_count, out_v=out_f, lse=w.lse,
+                                              workspace=w.workspace, chunk_tokens=w.chunk_tokens, events=events)
+
+    def pair(events=None):
+        w.call(events=events)
+        binding.tpla_value_up_projection(w.out, w_t, out_v=out_p)
+
+    fns = (("fused", fused), ("unfused_pair", pair))
+    for _ in range(warmup):
+        for _, fn in fns:
+            if flush_buf is not None:
+                flush_buf.sum()
+            fn()
+    torch.cuda.synchronize()
+    call = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)] for n, _ in fns}
+    tail = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)] for n, _ in fns}
+    for i in range(steps):
+        for n, fn in fns:
+            if flush_buf is not None:
+                flush_buf.sum()
+            call[n][i][0].record()
+            fn()
+            call[n][i][1].record()
+    for i in range(steps):
+        for n, fn in fns:
+            if flush_buf is not None:
+                flush_buf.sum()
+            e = tail[n][i]
+            fn(events=(e[0], e[1]))
+            e[2].record()
+    torch.cuda.synchronize()
+    ms = {n: [e[0].elapsed_time(e[1]) for e in call[n]] for n, _ in fns}
+    after = {n: [e[1].elapsed_time(e[2]) * 1e3 for e in tail[n]] for n, _ in fns}
+    a, b = out_f.cpu().numpy().astype(np.float64), out_p.cpu().numpy().astype(np.float64)
+    diff = float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+    nbytes = w.bytes + H * d_v * c.d_latent * 2 + B * H * d_v * 4
+    f_ms, p_ms = statistics.fmean(ms["fused"]), statistics.fmean(ms["unfused_pair"])
+    del w_t, out_f, out_p
+    return {"workload": c.name, "d_v": d_v, "weights": "bf16",
+            "fused_call_ms_mean": f_ms, "fused_call_ms_median": statistics.median(ms["fused"]),
+            "unfused_pair_ms_mean": p_ms, "unfused_pair_ms_median": statistics.median(ms["unfused_pair"]),
+            "after_decode_us_median": {n: statistics.median(v) for n, v in after.items()},
+            "algorithmic_bytes": nbytes, "fused_gbs": nbytes / (f_ms * 1e-3) / 1e9,
+            "fused_frac_of_peak": nbytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "max_abs_diff_vs_pair_rel_to_max": diff}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
@@ -776,6 +850,9 @@ def main():
     }
     head_case, head_shards = head.case, head.shard_count
     head_out, head_lse = head.out.cpu().numpy(), head.lse.cpu().numpy()
+    if not args.headline_only:
+        line["projected_decode"] = time_projected(head, args.extra_steps, args.warmup, not args.no_flush)
+        log(f"projected decode: {json.dumps(line['projected_decode'])}")
     append_case = None
     del head
     torch.cuda.empty_cache()
@@ -801,6 +878,9 @@ def main():
                                        "hbm_frac_of_peak": r["call_gbs"] / HBM_PEAK_GBS,
                                        "roofline": roofline_of(w, r)}
             extra_cpu[w.case.name] = (w.case, w.out.cpu().numpy(), w.lse.cpu().numpy())
+            if cfg == 2:
+                others[w.case.name]["projected_decode"] = time_projected(w, args.extra_steps, args.warmup,
+                                                                         not args.no_flush)
             if w.case.shards > 1 and not w.case.paged and cfg != 1:
                 others[w.case.name]["per_device_share"] = time_shard_calls(w, args.extra_steps, args.warmup,
                                                                            not args.no_flush)

@@ -50,7 +50,8 @@
 extern "C" {
 #endif
 
-#define TPLA_ABI_VERSION 4  /* 3: adds the prefill calls; 4: the allocation-free decode */
+#define TPLA_ABI_VERSION 5  /* 3: adds the prefill calls; 4: the allocation-free decode;
+                                  5: the decode with the fused value up-projection */
 
 typedef enum {
   TPLA_OK = 0,
@@ -207,6 +208,38 @@ int32_t tpla_decode_sharded_noalloc(const tpla_cache_desc_t* desc, const void* c
                                     const void* q_latent, const void* q_rope, float scale,
                                     int32_t num_shards, int32_t shard_begin, int32_t shard_count,
                                     float* out, float* lse, void* stream);
+
+/* TPLA decode with the value up-projection fused into its last step: the
+ * summed latent row of each (b, h) -- what tpla_decode_sharded writes to
+ * `out` -- is multiplied by that head's value rows of kv_b_proj on the GPU
+ * without being written to memory, and only the projected row is stored
+ * ([FR] Background / problem: kv_b_proj per head, o_proj rowwise, then the
+ * all-reduce; [REV] referee report, significance: matrix absorption):
+ *   out_v[b,h,:] = W_UV[h] . o[b,h,:]
+ * with o exactly the `out` of tpla_decode_sharded for the same arguments
+ * (so out_v equals tpla_decode_sharded followed by tpla_value_up_projection;
+ * for d_v <= 128 the two give the same bits).  For one device's shard subset
+ * out_v is that device's operand of the all-reduce.
+ *   w_dtype  TPLA_BF16 (fp32 weights: use the two calls)
+ *   w_uv     device, bf16 [heads, d_v, d_latent]: row v of head h maps the
+ *            latent to value component v
+ *   d_v      1 <= d_v <= 512
+ *   out_v    device, fp32 [batch, heads, d_v], fully overwritten; an empty
+ *            sequence gives 0
+ *   lse      as for tpla_decode_sharded, or NULL
+ * Every other argument, the workspace (tpla_workspace_size with the same
+ * arguments and opts) and the errors are those of tpla_decode_sharded_ex;
+ * d_latent must be a multiple of 16.  Alignment: w_uv and out_v 16 bytes.
+ * The o rows enter the product as a bf16 value plus its bf16 remainder (two
+ * products into one fp32 sum), as in tpla_value_up_projection. */
+int32_t tpla_decode_sharded_projected(const tpla_cache_desc_t* desc, const void* cache,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int32_t batch, int32_t heads, int32_t max_seq_len,
+                                      const void* q_latent, const void* q_rope, float scale,
+                                      int32_t num_shards, int32_t shard_begin, int32_t shard_count,
+                                      int32_t w_dtype, const void* w_uv, int32_t d_v,
+                                      float* out_v, float* lse, void* workspace, size_t workspace_bytes,
+                                      const tpla_decode_opts_t* opts, void* stream);
 
 /* Exact weight-absorbed MLA decode ([REV] referee report, significance:
  * matrix absorption; [FR] Tests / validation: G = 1 must equal head-parallel

@@ -29,7 +29,7 @@ EXPORTED = ["tpla_abi_version", "tpla_status_string", "tpla_last_error", "tpla_w
             "latent_cache_append", "tpla_decode_sharded", "tpla_decode_sharded_ex", "mla_decode_absorbed",
             "tpla_value_up_projection", "tpla_merge_context_parts", "latent_cache_append_normed",
             "mla_prefill_workspace_size", "mla_prefill_absorbed", "mla_prefill_absorbed_ex",
-            "tpla_decode_sharded_noalloc"]
+            "tpla_decode_sharded_noalloc", "tpla_decode_sharded_projected"]
 
 
 class TplaError(RuntimeError):
@@ -97,6 +97,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tpla_decode_sharded_ex.argtypes = decode_args + [ctypes.POINTER(DecodeOpts), _P]
     lib.tpla_decode_sharded_noalloc.restype = _I32
     lib.tpla_decode_sharded_noalloc.argtypes = decode_args[:-2] + [_P]
+    lib.tpla_decode_sharded_projected.restype = _I32
+    lib.tpla_decode_sharded_projected.argtypes = (decode_args[:13] + [_I32, _P, _I32] + decode_args[13:]
+                                                  + [ctypes.POINTER(DecodeOpts), _P])
     lib.mla_decode_absorbed.restype = _I32
     lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]
@@ -248,6 +251,43 @@ def tpla_decode_sharded_noalloc(desc: Desc, cache: torch.Tensor, block_table: to
                                            heads, max_seq_len, _ptr(q_latent), _ptr(q_rope), ctypes.c_float(scale),
                                            num_shards, shard_begin, shard_count, _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def tpla_decode_sharded_projected(desc: Desc, cache: torch.Tensor, block_table: torch.Tensor | None,
+                                  seq_lens: torch.Tensor, q_latent: torch.Tensor, q_rope: torch.Tensor, scale: float,
+                                  num_shards: int, max_seq_len: int, w_uv: torch.Tensor, shard_begin: int = 0,
+                                  shard_count: int | None = None, out_v: torch.Tensor | None = None,
+                                  lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                  want_lse: bool = True, chunk_tokens: int = 0, kernel: str = "auto", events=None,
+                                  stream=None, schedule: str = "auto"):
+    """TPLA decode with the value up-projection fused into the merge; w_uv bf16 [H, d_v, d_latent].
+    Returns (out_v [B, H, d_v] fp32, lse [B, shard_count, H] fp32 or None)."""
+    if shard_count is None:
+        shard_count = num_shards - shard_begin
+    batch, heads = int(q_latent.shape[0]), int(q_latent.shape[1])
+    dev = q_latent.device
+    if seq_lens.dtype != torch.int32 or (block_table is not None and block_table.dtype != torch.int32):
+        raise ValueError("seq_lens and block_table must be int32")
+    if w_uv.dim() != 3 or int(w_uv.shape[0]) != heads or int(w_uv.shape[2]) != desc.d_latent:
+        raise ValueError("w_uv must be [heads, d_v, d_latent]")
+    d_v = int(w_uv.shape[1])
+    w_dtype = DTYPES["bf16"] if w_uv.dtype == torch.bfloat16 else DTYPES["f32"]
+    if out_v is None:
+        out_v = torch.empty((batch, heads, d_v), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((batch, shard_count, heads), dtype=torch.float32, device=dev)
+    need = workspace_size(desc, batch, heads, num_shards, shard_count, max_seq_len, chunk_tokens, kernel, schedule)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    lib = load_library()
+    cdesc = desc.c()
+    _check(lib.tpla_decode_sharded_projected(ctypes.byref(cdesc), _ptr(cache), _ptr(block_table), _ptr(seq_lens),
+                                             batch, heads, max_seq_len, _ptr(q_latent), _ptr(q_rope),
+                                             ctypes.c_float(scale), num_shards, shard_begin, shard_count, w_dtype,
+                                             _ptr(w_uv), d_v, _ptr(out_v), _ptr(lse), _ptr(workspace),
+                                             workspace.numel(), _opts(chunk_tokens, kernel, events, schedule),
+                                             _stream(stream)))
+    return out_v, lse
 
 
 def mla_decode_absorbed(desc: Desc, cache: torch.Tensor, block_table: torch.Tensor | None, seq_lens: torch.Tensor,

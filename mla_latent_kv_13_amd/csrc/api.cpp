@@ -244,6 +244,14 @@ struct PrefillRows {
   int32_t sequences;
 };
 
+// The value up-projection fused into the merge (tpla_decode_sharded_projected).
+struct Projection {
+  int32_t w_dtype;
+  const void* w_uv;
+  int32_t d_v;
+  float* out_v;
+};
+
 // One decode call over `batch` query rows.  Decode: row b is sequence b over seq_lens[b] tokens.
 // Prefill (pf non-null): `batch` new-token rows of pf->sequences sequences, each over its causal
 // prefix of the cache (the row map is built on the device first).
@@ -251,17 +259,29 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
                     const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len, const void* q_latent,
                     const void* q_rope, float scale, int32_t num_shards, int32_t shard_begin, int32_t shard_count,
                     float* out, float* lse, void* workspace, size_t workspace_bytes, const tpla_decode_opts_t* opts,
-                    void* stream_ptr, const PrefillRows* pf = nullptr) {
+                    void* stream_ptr, const PrefillRows* pf = nullptr, const Projection* proj = nullptr) {
   Plan plan;
   int32_t st = make_plan(d, batch, heads, num_shards, shard_count, max_seq_len, opts, &plan, pf != nullptr);
   if (st != TPLA_OK) return st;
   const int32_t sequences = pf ? pf->sequences : batch;
   if (shard_begin < 0 || shard_begin + shard_count > num_shards)
     return fail(TPLA_ERR_INVALID_ARGUMENT, "shard range [%d, %d) outside [0, %d)", shard_begin, shard_begin + shard_count, num_shards);
-  if (!cache || !seq_lens || !q_latent || !out || (d->d_rope > 0 && !q_rope))
+  if (!cache || !seq_lens || !q_latent || (!proj && !out) || (d->d_rope > 0 && !q_rope))
     return fail(TPLA_ERR_INVALID_ARGUMENT, "a required device pointer is NULL");
-  if (!aligned(cache, 16) || !aligned(q_latent, 16) || (q_rope && !aligned(q_rope, 16)) || !aligned(out, 16))
+  if (!aligned(cache, 16) || !aligned(q_latent, 16) || (q_rope && !aligned(q_rope, 16)) || (out && !aligned(out, 16)))
     return fail(TPLA_ERR_INVALID_ARGUMENT, "cache, q_latent, q_rope and out must be 16-byte aligned");
+  if (proj) {
+    if (proj->w_dtype != TPLA_BF16)
+      return fail(TPLA_ERR_UNSUPPORTED, "the fused up-projection takes bf16 weights (w_dtype %d); fp32 weights: "
+                  "tpla_decode_sharded then tpla_value_up_projection", proj->w_dtype);
+    if (proj->d_v < 1) return fail(TPLA_ERR_INVALID_ARGUMENT, "d_v must be >= 1");
+    if (proj->d_v > 512 || d->d_latent % 16 != 0)
+      return fail(TPLA_ERR_UNSUPPORTED, "the fused up-projection needs d_v <= 512 and d_latent a multiple of 16 (d_v=%d, d_latent=%d)",
+                  proj->d_v, d->d_latent);
+    if (!proj->w_uv || !proj->out_v) return fail(TPLA_ERR_INVALID_ARGUMENT, "w_uv and out_v must not be NULL");
+    if (!aligned(proj->w_uv, 16) || !aligned(proj->out_v, 16))
+      return fail(TPLA_ERR_INVALID_ARGUMENT, "w_uv and out_v must be 16-byte aligned");
+  }
   if (!(scale == scale)) return fail(TPLA_ERR_INVALID_ARGUMENT, "scale is NaN");
   if (block_table == nullptr) {
     if (d->num_pages < sequences || d->page_size < max_seq_len)
@@ -362,6 +382,12 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
   M.wht = wht ? 1 : 0;
   M.out = out;
   M.lse = lse;
+  if (proj) {
+    e = tpla::launch_merge_project(M, static_cast<const uint16_t*>(proj->w_uv), proj->d_v, proj->out_v,
+                                   device_shape().xcds, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge with up-projection launch");
+    return ok();
+  }
   e = tpla::launch_merge(M, stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();
@@ -528,6 +554,17 @@ int32_t tpla_decode_sharded_noalloc(const tpla_cache_desc_t* desc, const void* c
   if (sst != TPLA_OK) return sst;
   return decode_impl(desc, cache, block_table, seq_lens, batch, heads, max_seq_len, q_latent, q_rope, scale, num_shards,
                      shard_begin, shard_count, out, lse, ws, kScratchBytes, nullptr, stream);
+}
+
+int32_t tpla_decode_sharded_projected(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,
+                                      const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t max_seq_len,
+                                      const void* q_latent, const void* q_rope, float scale, int32_t num_shards,
+                                      int32_t shard_begin, int32_t shard_count, int32_t w_dtype, const void* w_uv,
+                                      int32_t d_v, float* out_v, float* lse, void* workspace, size_t workspace_bytes,
+                                      const tpla_decode_opts_t* opts, void* stream) {
+  const Projection proj{w_dtype, w_uv, d_v, out_v};
+  return decode_impl(desc, cache, block_table, seq_lens, batch, heads, max_seq_len, q_latent, q_rope, scale, num_shards,
+                     shard_begin, shard_count, nullptr, lse, workspace, workspace_bytes, opts, stream, nullptr, &proj);
 }
 
 int32_t mla_decode_absorbed(const tpla_cache_desc_t* desc, const void* cache, const int32_t* block_table,

@@ -77,6 +77,11 @@ void mfma_plan_info(int w, int heads, int* head_groups, int* wgs_per_cu);
 // Largest number of cache pages one chunk of the MFMA kernel may span.
 int mfma_max_chunk_pages();
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
+// The merge with the value up-projection fused in: out_v[b,h,:] = W_UV[h] . (the row launch_merge
+// would write to a.out, which is not written); bf16 weights [heads, d_v, d_latent], d_latent a
+// multiple of 16, 1 <= d_v <= 512.
+hipError_t launch_merge_project(const MergeLaunch& a, const uint16_t* w_uv, int d_v, float* out_v, int xcds,
+                                hipStream_t stream);
 // tile_prefix[b] = sum over b' < b of ceil(seq_lens[b'] / 32), b = 0..batch.
 hipError_t launch_tile_prefix(const int* seq_lens, int batch, int* tile_prefix, hipStream_t stream);
 // Query rows of a prefill call: row r in [query_start[b], query_start[b+1]) belongs to sequence

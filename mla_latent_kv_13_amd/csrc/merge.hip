@@ -9,6 +9,8 @@
 //   cache the summed row is rotated back, out = H y.
 // rotate_query: q~ = H q_lat for a Hadamard-rotated cache, so that logits are unchanged at G = 1
 //   (TPLA abstract: an orthogonal transform before slicing).
+#include <algorithm>
+
 #include "kernels.h"
 #include "tpla_device.h"
 
@@ -133,15 +135,12 @@ __device__ __forceinline__ int pad_log2(int nr, int p) {
   return 32 - __clz(m - 1);
 }
 
-// E > 0: the one-pass path (E, P, S as above) is compiled in for waves whose partials fit it.
+// The summed latent row y of (sequence b, head h), d_latent floats at y (16-byte aligned; LDS),
+// and the log-sum-exps of the computed shards (when a.lse is set).  Wave-local.  E > 0: the
+// one-pass path (E, P, S as above) is compiled in for waves whose partials fit it.
 template <int V, int E, int P, int S>
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
+__device__ __forceinline__ void merge_row(const MergeLaunch& a, int b, int h, int lane, float* y) {
   typedef typename Vec<V>::T vec_t;
-  __shared__ __attribute__((aligned(64))) float ybuf[kMergeWaves][kMaxLatent];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = blockIdx.x * kMergeWaves + wv, b = blockIdx.y;
-  if (h >= a.heads) return;  // the rest of this kernel is wave-local
-  float* y = ybuf[wv];
   const int lo = a.shard_begin * a.w, hi = lo + a.shard_count * a.w;
   for (int j = lane; j < a.d_latent; j += 64)
     if (j < lo || j >= hi) y[j] = 0.f;  // latent columns of shards that were not computed
@@ -156,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
                                   min(per, a.shard_count - s0), [&] {
                                     return (a.seq_lens[b] + a.chunk_tokens - 1) / a.chunk_tokens;
                                   }, y);
-        goto rows_done;
+        return;
       }
     }
   }
@@ -185,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
       for (int s0 = 0; s0 < a.shard_count; s0 += per)
         merge_one_pass<E, P, S>(a, b, h, lane, slot0, max(nv, 1), lg2, s0, min(per, a.shard_count - s0),
                                 [&] { return nv; }, y);
-      goto rows_done;
+      return;
     }
   }
 
@@ -236,7 +235,27 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
       a.lse[(static_cast<int64_t>(b) * a.shard_count + sl) * a.heads + h] = nv > 0 ? M + logf(Z) : -INFINITY;
   }
   }
-rows_done:
+}
+
+// dst = H y for a row of n values (n a power of two <= 1024); dst may be y itself.
+__device__ __forceinline__ void rotate_row(const float* y, float* dst, int n, int lane) {
+  switch (n <= 64 ? 1 : n / 64) {
+    case 1: rotate_out<1>(y, dst, n, lane); break;
+    case 2: rotate_out<2>(y, dst, n, lane); break;
+    case 4: rotate_out<4>(y, dst, n, lane); break;
+    case 8: rotate_out<8>(y, dst, n, lane); break;
+    default: rotate_out<16>(y, dst, n, lane); break;
+  }
+}
+
+template <int V, int E, int P, int S>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
+  __shared__ __attribute__((aligned(64))) float ybuf[kMergeWaves][kMaxLatent];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kMergeWaves + wv, b = blockIdx.y;
+  if (h >= a.heads) return;  // the rest of this kernel is wave-local
+  float* y = ybuf[wv];
+  merge_row<V, E, P, S>(a, b, h, lane, y);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // this wave's LDS row is complete
   __builtin_amdgcn_wave_barrier();
 
@@ -246,12 +265,146 @@ rows_done:
       reinterpret_cast<float4*>(dst)[j] = reinterpret_cast<const float4*>(y)[j];
     return;
   }
-  switch (a.d_latent <= 64 ? 1 : a.d_latent / 64) {
-    case 1: rotate_out<1>(y, dst, a.d_latent, lane); break;
-    case 2: rotate_out<2>(y, dst, a.d_latent, lane); break;
-    case 4: rotate_out<4>(y, dst, a.d_latent, lane); break;
-    case 8: rotate_out<8>(y, dst, a.d_latent, lane); break;
-    default: rotate_out<16>(y, dst, a.d_latent, lane); break;
+  rotate_row(y, dst, a.d_latent, lane);
+}
+
+// Merge with the value up-projection fused in: out_v[b, h, :] = W_UV[h] . o[b, h, :], o being the
+// row merge_kernel would write (value rows of kv_b_proj applied after latent attention: automated
+// review of the TPLA paper, referee report "significance", matrix absorption; feature request on
+// latent-cache sharding, "Background / problem": kv_b_proj per head, o_proj rowwise, then the
+// all-reduce).  The merged rows never leave the CU.
+//
+// Workgroup = one head h and kProjRows consecutive sequences; wave i merges sequences b0 + i,
+// b0 + i + kProjWaves, ... into LDS rows i, i + kProjWaves, ... (rotated back in place under the
+// Hadamard transform).  Then the waves apply W_UV[h]
+// on the matrix cores as the up-projection kernel does: 32x32x16 bf16 MFMAs, rows of o entering as
+// bf16(o) plus the bf16 remainder, wave (vt, kq) taking value columns [32 vt, 32 vt + 32) over
+// the k-part kq of kparts equal parts of the latent, the k-parts' tiles added in LDS in kq order.
+// With at most four value tiles (d_v <= 128) there are four k-parts split as that kernel splits
+// them, so each output is the same sum in the same order.  MFMA rows past kProjRows are zero and
+// never stored.  A wave requests the weight operands of its first 8 k-steps as soon as its row is merged.
+constexpr int kProjWaves = 16;
+constexpr int kProjRows = 16;  // a multiple of kProjWaves and of 8, at most 32
+constexpr int kProjThreads = 64 * kProjWaves;
+constexpr int kProjAcc = kProjRows / 2;  // accumulators of a lane that hold rows < kProjRows
+
+struct ProjectArgs {
+  const uint16_t* w;  // bf16 [heads, d_v, d_latent]
+  int d_v;
+  int vp;             // waves per k-part: a power of two >= ceil(d_v / 32), at least 4, at most kProjWaves
+  float* out_v;       // fp32 [batch, heads, d_v]
+  int xcds;
+};
+
+template <int V, int E, int P, int S>
+__global__ __launch_bounds__(kProjThreads) void merge_project_kernel(MergeLaunch a, ProjectArgs p) {
+  extern __shared__ __attribute__((aligned(16))) float rows_s[];  // [kProjRows][d_latent + 4], then the k-part tiles
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // Workgroup id -> (head, batch tile).  Ids are dealt to the XCDs round-robin; the batch tiles of
+  // head h get ids = h (mod xcds), so they run on one XCD and read W_UV[h] through its L2.
+  const int btiles = (a.batch + kProjRows - 1) / kProjRows;
+  const int xcd = blockIdx.x % p.xcds, k = blockIdx.x / p.xcds;
+  const int h = (k / btiles) * p.xcds + xcd;
+  if (h >= a.heads) return;  // uniform over the workgroup
+  const int b0 = (k % btiles) * kProjRows;
+  const int ys = a.d_latent + 4;  // floats per LDS row: rows start 16 bytes (4 banks) apart
+  const int vt = wv & (p.vp - 1), kq = wv / p.vp, kparts = kProjWaves / p.vp;
+  const int ksteps = a.d_latent / 16;
+  const int kb = kq * ksteps / kparts, ke = (kq + 1) * ksteps / kparts;
+  const bool active = vt * 32 < p.d_v;
+  const int half = lane >> 5, l32 = lane & 31;
+  // B operand of k-step s: lane l holds W_UV[h][v0 + l % 32][16 s + 8 (l / 32) + i], i < 8 (rows
+  // past d_v repeat the last one, k-steps past the latent the last one; neither is used).
+  const uint16_t* wrow = p.w + (static_cast<int64_t>(h) * p.d_v + min(vt * 32 + l32, p.d_v - 1)) * a.d_latent + 8 * half;
+  uint4 wf[8];
+  auto load_w = [&](int g) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) wf[s] = *reinterpret_cast<const uint4*>(wrow + 16 * min(g + s, ksteps - 1));
+  };
+
+  for (int i = wv; i < kProjRows; i += kProjWaves) {
+    float* y = rows_s + i * ys;
+    const int b = b0 + i;
+    const bool last = i + kProjWaves >= kProjRows;
+    if (b < a.batch) {
+      merge_row<V, E, P, S>(a, b, h, lane, y);
+      if (active && last) load_w(kb);  // in flight during the rotation and the wait for the other rows
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // this wave's LDS row is complete
+      __builtin_amdgcn_wave_barrier();
+      if (a.wht) rotate_row(y, y, a.d_latent, lane);
+    } else {
+      if (active && last) load_w(kb);
+      for (int j = lane; j < a.d_latent; j += 64) y[j] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  floatx16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  if (active) {
+    const float* arow = rows_s + l32 * ys + 8 * half;  // A operand: lane l holds o[b0 + l % 32][16 s + 8 (l / 32) + i]
+    for (int g = kb; g < ke; g += 8) {
+      uint4 cur[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) cur[s] = wf[s];
+      if (g + 8 < ke) load_w(g + 8);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (g + s < ke) {
+          float x[8];
+          if (l32 < kProjRows) {
+            const float4 a0 = *reinterpret_cast<const float4*>(arow + 16 * (g + s));
+            const float4 a1 = *reinterpret_cast<const float4*>(arow + 16 * (g + s) + 4);
+            x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+            x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.f;
+          }
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+            const float r0 = x[2 * i] - bf16_to_f32(static_cast<uint16_t>(hi[i] & 0xffffu));
+            const float r1 = x[2 * i + 1] - bf16_to_f32(static_cast<uint16_t>(hi[i] >> 16));
+            lo[i] = pack_bf16x2(r0, r1);
+          }
+          const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, cur[s]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3])), bw, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), bw, acc, 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done reading the rows
+  // Accumulator r of lane l is D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]: rows < kProjRows are
+  // r < kProjAcc, kProjAcc / 4 groups of four.
+  constexpr int NG = kProjAcc / 4;
+  floatx4_t* part = reinterpret_cast<floatx4_t*>(rows_s);  // [vp][kparts - 1][NG][64]
+  if (active && kq > 0) {
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+      part[((vt * (kparts - 1) + kq - 1) * NG + j) * 64 + lane] = floatx4_t{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+  }
+  __syncthreads();
+  if (!active || kq > 0) return;
+  for (int q = 0; q < kparts - 1; ++q) {
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const floatx4_t t = part[((vt * (kparts - 1) + q) * NG + j) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * j + e] += t[e];
+    }
+  }
+  const int vv = vt * 32 + l32;
+  if (vv >= p.d_v) return;
+#pragma unroll
+  for (int r = 0; r < kProjAcc; ++r) {
+    const int bb = b0 + 8 * (r >> 2) + 4 * half + (r & 3);
+    if (bb < a.batch) p.out_v[(static_cast<int64_t>(bb) * a.heads + h) * p.d_v + vv] = acc[r];
   }
 }
 
@@ -419,6 +572,33 @@ __global__ __launch_bounds__(kThreads) void tile_prefix_kernel(const int* __rest
   if (threadIdx.x == kThreads - 1) prefix[batch] = sums[kThreads - 1];
 }
 
+// Merge kernel variants <V, E, P, S>, indexed by merge_variant().
+#define TPLA_MERGE_VARIANTS(X)                                                                  \
+  X(0, 4, 0, 1, 1) X(1, 1, 0, 1, 1) X(2, 4, 2, 1, 4) X(3, 4, 2, 1, 8) X(4, 4, 1, 1, 4)           \
+  X(5, 4, 1, 1, 8) X(6, 4, 1, 1, 16) X(7, 4, 1, 2, 4) X(8, 4, 1, 2, 8) X(9, 4, 1, 2, 16)         \
+  X(10, 4, 1, 4, 4) X(11, 4, 1, 4, 8) X(12, 4, 1, 4, 16)
+
+// One-pass shape: float4 per lane per row (E) or rows per load step (P) from the slice width;
+// steps S: the fewest of 4, 8 and 16 / E that hold every chunk row of all shards under the
+// chunked schedule (else 16 / E, shards in several passes), and 16 / E under the balanced
+// schedule, where the rows per sequence vary.
+int merge_variant(const MergeLaunch& a) {
+  const int nvec = a.w / 4;
+  const int e = a.w % 4 != 0 || nvec > 128 ? 0 : (nvec > 64 ? 2 : 1);
+  const int pr = nvec > 32 ? 1 : (nvec > 16 ? 2 : 4);
+  int steps = 16 / max(e, 1);
+  if (a.sched == 0) {
+    int n2 = pr;
+    while (n2 < a.num_chunks) n2 <<= 1;
+    const int need = a.shard_count * n2 / pr;
+    steps = need <= 4 ? 4 : (need <= 8 ? 8 : steps);
+  }
+  const int si = steps == 4 ? 0 : (steps == 8 ? 1 : 2);
+  if (e == 0) return a.w % 4 == 0 ? 0 : 1;
+  if (e == 2) return steps == 4 ? 2 : 3;
+  return (pr == 1 ? 4 : (pr == 2 ? 7 : 10)) + si;
+}
+
 }  // namespace
 
 hipError_t launch_tile_prefix(const int* seq_lens, int batch, int* tile_prefix, hipStream_t stream) {
@@ -430,28 +610,60 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
   if (a.d_latent > kMaxLatent) return hipErrorInvalidValue;
   if (a.wht && (a.d_latent & (a.d_latent - 1)) != 0) return hipErrorInvalidValue;
   const dim3 grid((a.heads + kMergeWaves - 1) / kMergeWaves, a.batch);
-  // One-pass shape: float4 per lane per row (E) or rows per load step (P) from the slice width;
-  // steps S: the fewest of 4, 8 and 16 / E that hold every chunk row of all shards under the
-  // chunked schedule (else 16 / E, shards in several passes), and 16 / E under the balanced
-  // schedule, where the rows per sequence vary.
-  const int nvec = a.w / 4;
-  const int e = a.w % 4 != 0 || nvec > 128 ? 0 : (nvec > 64 ? 2 : 1);
-  const int pr = nvec > 32 ? 1 : (nvec > 16 ? 2 : 4);
-  int steps = 16 / max(e, 1);
-  if (a.sched == 0) {
-    int n2 = pr;
-    while (n2 < a.num_chunks) n2 <<= 1;
-    const int need = a.shard_count * n2 / pr;
-    steps = need <= 4 ? 4 : (need <= 8 ? 8 : steps);
-  }
   using K = void (*)(MergeLaunch);
-  K kern;
-  if (e == 0) kern = a.w % 4 == 0 ? merge_kernel<4, 0, 1, 1> : merge_kernel<1, 0, 1, 1>;
-  else if (e == 2) kern = steps == 4 ? merge_kernel<4, 2, 1, 4> : merge_kernel<4, 2, 1, 8>;
-  else if (pr == 1) kern = steps == 4 ? merge_kernel<4, 1, 1, 4> : steps == 8 ? merge_kernel<4, 1, 1, 8> : merge_kernel<4, 1, 1, 16>;
-  else if (pr == 2) kern = steps == 4 ? merge_kernel<4, 1, 2, 4> : steps == 8 ? merge_kernel<4, 1, 2, 8> : merge_kernel<4, 1, 2, 16>;
-  else kern = steps == 4 ? merge_kernel<4, 1, 4, 4> : steps == 8 ? merge_kernel<4, 1, 4, 8> : merge_kernel<4, 1, 4, 16>;
+  K kern = nullptr;
+  switch (merge_variant(a)) {
+#define TPLA_X(i, V, E, P, S) \
+  case i: kern = merge_kernel<V, E, P, S>; break;
+    TPLA_MERGE_VARIANTS(TPLA_X)
+#undef TPLA_X
+    default: return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_project(const MergeLaunch& a, const uint16_t* w_uv, int d_v, float* out_v, int xcds,
+                                hipStream_t stream) {
+  if (a.d_latent > kMaxLatent || a.d_latent % 16 != 0 || d_v < 1 || d_v > 32 * kProjWaves || xcds < 1)
+    return hipErrorInvalidValue;
+  if (a.wht && (a.d_latent & (a.d_latent - 1)) != 0) return hipErrorInvalidValue;
+  ProjectArgs p;
+  p.w = w_uv;
+  p.d_v = d_v;
+  p.vp = 4;
+  while (p.vp * 32 < d_v) p.vp <<= 1;
+  p.out_v = out_v;
+  p.xcds = xcds;
+  const int btiles = (a.batch + kProjRows - 1) / kProjRows;
+  const int64_t blocks = static_cast<int64_t>((a.heads + xcds - 1) / xcds) * xcds * btiles;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int kparts = kProjWaves / p.vp;
+  const size_t lds = std::max<size_t>(static_cast<size_t>(kProjRows) * (a.d_latent + 4) * sizeof(float),
+                                      static_cast<size_t>(p.vp) * (kparts - 1) * (kProjAcc / 4) * 64 * sizeof(floatx4_t));
+  // Sixteen waves per workgroup leave 128 registers per lane: the one-pass shapes holding 32 or
+  // more float4 per lane (S E = 16) would spill, so they run with half the steps (sequences with
+  // more partials than that take the general loop).
+  using K = void (*)(MergeLaunch, ProjectArgs);
+  K kern = nullptr;
+  switch (merge_variant(a)) {
+    case 0: kern = merge_project_kernel<4, 0, 1, 1>; break;
+    case 1: kern = merge_project_kernel<1, 0, 1, 1>; break;
+    case 2: case 3: kern = merge_project_kernel<4, 2, 1, 4>; break;
+    case 4: kern = merge_project_kernel<4, 1, 1, 4>; break;
+    case 5: case 6: kern = merge_project_kernel<4, 1, 1, 8>; break;
+    case 7: kern = merge_project_kernel<4, 1, 2, 4>; break;
+    case 8: case 9: kern = merge_project_kernel<4, 1, 2, 8>; break;
+    case 10: kern = merge_project_kernel<4, 1, 4, 4>; break;
+    case 11: case 12: kern = merge_project_kernel<4, 1, 4, 8>; break;
+    default: return hipErrorInvalidValue;
+  }
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kProjThreads), lds, stream, a, p);
   return hipGetLastError();
 }
 

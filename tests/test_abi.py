@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert binding.abi_version() == 4
+    assert binding.abi_version() == 5
     assert lib.tpla_status_string(3) == b"TPLA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -127,6 +127,46 @@ def test_decode_validation_before_launch(lib, kw, status):
     st, msg = _decode_raw(lib, DSV3, **kw)
     assert st == status, (st, msg)
     assert msg
+
+
+def _projected_raw(lib, desc, **kw):
+    """tpla_decode_sharded_projected with fake (never dereferenced) device addresses; only for
+    arguments that validation rejects before anything is enqueued."""
+    a = dict(cache=0x10000, block_table=0x20000, seq_lens=0x30000, batch=2, heads=128, max_seq_len=4096,
+             q_latent=0x40000, q_rope=0x50000, scale=0.1, num_shards=2, shard_begin=0, shard_count=2,
+             w_dtype=1, w_uv=0x80000, d_v=128, out_v=0x60000, lse=0, workspace=0x70000, workspace_bytes=1 << 40)
+    a.update(kw)
+    cdesc = desc.c()
+    p = ctypes.c_void_p
+    st = lib.tpla_decode_sharded_projected(
+        ctypes.byref(cdesc), p(a["cache"]), p(a["block_table"] or None), p(a["seq_lens"]), a["batch"], a["heads"],
+        a["max_seq_len"], p(a["q_latent"]), p(a["q_rope"]), ctypes.c_float(a["scale"]), a["num_shards"],
+        a["shard_begin"], a["shard_count"], a["w_dtype"], p(a["w_uv"] or None), a["d_v"], p(a["out_v"] or None),
+        p(a["lse"] or None), p(a["workspace"]), a["workspace_bytes"], None, None)
+    return st, lib.tpla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w_dtype=0), 2),                        # fp32 weights: the two-call path
+    (dict(d_v=513), 2),
+    (dict(d_v=0), 1),
+    (dict(w_uv=0), 1),
+    (dict(out_v=0), 1),
+    (dict(w_uv=0x80008), 1),                     # misaligned weights
+    (dict(out_v=0x60004), 1),                    # misaligned output
+    (dict(workspace_bytes=16), 3),
+    (dict(shard_begin=1, shard_count=2), 1),
+])
+def test_projected_decode_validation_before_launch(lib, kw, status):
+    st, msg = _projected_raw(lib, DSV3, **kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_projected_decode_needs_latent_multiple_of_16(lib):
+    d40 = binding.Desc("bf16", 40, 8, 64, 10, 16, "identity")
+    st, msg = _projected_raw(lib, d40, num_shards=1, shard_count=1, heads=4)
+    assert st == 2 and "multiple of 16" in msg
 
 
 def test_bad_descriptor(lib):
