@@ -37,9 +37,10 @@
 // differ between tokens t and t+2.
 //
 // Cache layouts: LAYOUT 0 = contiguous (sequence b owns rows b*page_size...), 1 = paged with
-// page_size a multiple of 32 (a tile never straddles a page), 2 = any other paging.  In layouts
-// 0 and 1 a full tile is 32 consecutive rows, so each lane's DMA source is a fixed byte offset
-// from one wave-uniform row address.
+// page_size a power of two of at least 32 (a tile never straddles a page, and the page of a
+// token is a shift away), 2 = any other paging.  In layouts 0 and 1 a full tile is 32
+// consecutive rows, so each lane's DMA source is a fixed byte offset from one wave-uniform row
+// address, which layout 1 forms in scalar registers from the tile's page number.
 #include <type_traits>
 
 #include "kernels.h"
@@ -176,7 +177,8 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   const int page_size = a.page_size;
 
   int* pages = reinterpret_cast<int*>(lds + C::PAGES_OFF);
-  const int first_page = LAYOUT ? (page_shift >= 0 ? (t_begin >> page_shift) : t_begin / page_size) : 0;
+  const int first_page = LAYOUT == 1 ? (t_begin >> page_shift)
+                         : (LAYOUT ? (page_shift >= 0 ? (t_begin >> page_shift) : t_begin / page_size) : 0);
   if constexpr (LAYOUT != 0) {
     const int last_page = page_shift >= 0 ? ((t_end - 1) >> page_shift) : (t_end - 1) / page_size;
     const int* bt = a.block_table + static_cast<int64_t>(bs) * a.max_pages_per_seq + first_page;
@@ -206,8 +208,9 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     if constexpr (LAYOUT == 0) {
       return static_cast<int64_t>(bs) * page_size + t;
     } else {
-      const int pi = page_shift >= 0 ? (t >> page_shift) : t / page_size;
-      const int off = page_shift >= 0 ? (t & (page_size - 1)) : t - pi * page_size;
+      const bool sh = LAYOUT == 1 || page_shift >= 0;
+      const int pi = sh ? (t >> page_shift) : t / page_size;
+      const int off = sh ? (t & (page_size - 1)) : t - pi * page_size;
       return static_cast<int64_t>(pages[pi - first_page]) * page_size + off;
     }
   };
@@ -217,7 +220,16 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     const uint32_t dst = lds_base + stage * C::TILE_BYTES;
     if (LAYOUT != 2 && t0 + kNT <= t_end) {
       // 32 consecutive rows: one uniform base, per-lane constant offsets
-      const void* base = uniform_ptr(row_addr(row_of(t0)));
+      const void* base;
+      if constexpr (LAYOUT == 1) {
+        // power-of-two pages of at least 32 rows: the tile sits in one page; its address is
+        // formed in scalar registers from the page number
+        const int pg = __builtin_amdgcn_readfirstlane(pages[(t0 >> page_shift) - first_page]);
+        const int64_t row = (static_cast<int64_t>(pg) << page_shift) + (t0 & (page_size - 1));
+        base = cache + row * (D * 2);
+      } else {
+        base = uniform_ptr(row_addr(row_of(t0)));
+      }
 #pragma unroll
       for (int k = 0; k < C::PER_MAX; ++k) {
         if (C::REM != 0 && k >= n_pieces) break;
@@ -592,7 +604,7 @@ hipError_t launch_one(const DecodeLaunch& a, hipStream_t stream) {
 template <int W, int DR, int HB, int KS, int STQ>
 hipError_t launch_layout(const DecodeLaunch& a, hipStream_t stream) {
   if (a.block_table == nullptr) return launch_one<W, DR, HB, KS, STQ, 0>(a, stream);
-  if (a.page_size % kNT == 0) return launch_one<W, DR, HB, KS, STQ, 1>(a, stream);
+  if (a.page_size % kNT == 0 && (a.page_size & (a.page_size - 1)) == 0) return launch_one<W, DR, HB, KS, STQ, 1>(a, stream);
   return launch_one<W, DR, HB, KS, STQ, 2>(a, stream);
 }
 
