@@ -12,6 +12,7 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "project.h"
 #include "tpla_device.h"
 
 namespace tpla {
@@ -269,143 +270,38 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
 }
 
 // Merge with the value up-projection fused in: out_v[b, h, :] = W_UV[h] . o[b, h, :], o being the
-// row merge_kernel would write (value rows of kv_b_proj applied after latent attention: automated
-// review of the TPLA paper, referee report "significance", matrix absorption; feature request on
-// latent-cache sharding, "Background / problem": kv_b_proj per head, o_proj rowwise, then the
-// all-reduce).  The merged rows never leave the CU.
-//
-// Workgroup = one head h and kProjRows consecutive sequences; wave i merges sequences b0 + i,
-// b0 + i + kProjWaves, ... into LDS rows i, i + kProjWaves, ... (rotated back in place under the
-// Hadamard transform).  Then the waves apply W_UV[h]
-// on the matrix cores as the up-projection kernel does: 32x32x16 bf16 MFMAs, rows of o entering as
-// bf16(o) plus the bf16 remainder, wave (vt, kq) taking value columns [32 vt, 32 vt + 32) over
-// the k-part kq of kparts equal parts of the latent, the k-parts' tiles added in LDS in kq order.
-// With at most four value tiles (d_v <= 128) there are four k-parts split as that kernel splits
-// them, so each output is the same sum in the same order.  MFMA rows past kProjRows are zero and
-// never stored.  A wave requests the weight operands of its first 8 k-steps as soon as its row is merged.
-constexpr int kProjWaves = 16;
-constexpr int kProjRows = 16;  // a multiple of kProjWaves and of 8, at most 32
-constexpr int kProjThreads = 64 * kProjWaves;
-constexpr int kProjAcc = kProjRows / 2;  // accumulators of a lane that hold rows < kProjRows
-
-struct ProjectArgs {
-  const uint16_t* w;  // bf16 [heads, d_v, d_latent]
-  int d_v;
-  int vp;             // waves per k-part: a power of two >= ceil(d_v / 32), at least 4, at most kProjWaves
-  float* out_v;       // fp32 [batch, heads, d_v]
-  int xcds;
-};
-
+// row merge_kernel would write (the projection and its sources: project.h).  The merged rows
+// never leave the CU.  Workgroup = one head h and kProjRows consecutive sequences; wave i merges
+// sequences b0 + i, b0 + i + kProjWaves, ... into LDS rows i, i + kProjWaves, ... (rotated back in
+// place under the Hadamard transform), requesting its weight operands as soon as its last row is
+// merged; then the waves apply W_UV[h] to the rows.
 template <int V, int E, int P, int S>
 __global__ __launch_bounds__(kProjThreads) void merge_project_kernel(MergeLaunch a, ProjectArgs p) {
   extern __shared__ __attribute__((aligned(16))) float rows_s[];  // [kProjRows][d_latent + 4], then the k-part tiles
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // Workgroup id -> (head, batch tile).  Ids are dealt to the XCDs round-robin; the batch tiles of
-  // head h get ids = h (mod xcds), so they run on one XCD and read W_UV[h] through its L2.
-  const int btiles = (a.batch + kProjRows - 1) / kProjRows;
-  const int xcd = blockIdx.x % p.xcds, k = blockIdx.x / p.xcds;
-  const int h = (k / btiles) * p.xcds + xcd;
-  if (h >= a.heads) return;  // uniform over the workgroup
-  const int b0 = (k % btiles) * kProjRows;
-  const int ys = a.d_latent + 4;  // floats per LDS row: rows start 16 bytes (4 banks) apart
-  const int vt = wv & (p.vp - 1), kq = wv / p.vp, kparts = kProjWaves / p.vp;
-  const int ksteps = a.d_latent / 16;
-  const int kb = kq * ksteps / kparts, ke = (kq + 1) * ksteps / kparts;
-  const bool active = vt * 32 < p.d_v;
-  const int half = lane >> 5, l32 = lane & 31;
-  // B operand of k-step s: lane l holds W_UV[h][v0 + l % 32][16 s + 8 (l / 32) + i], i < 8 (rows
-  // past d_v repeat the last one, k-steps past the latent the last one; neither is used).
-  const uint16_t* wrow = p.w + (static_cast<int64_t>(h) * p.d_v + min(vt * 32 + l32, p.d_v - 1)) * a.d_latent + 8 * half;
+  int h, b0;
+  if (!proj_unit(a.batch, a.heads, p.xcds, h, b0)) return;  // uniform over the workgroup
+  const int ys = a.d_latent + 4;
+  const ProjWave pw(p, h, a.d_latent, wv, lane);
   uint4 wf[8];
-  auto load_w = [&](int g) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) wf[s] = *reinterpret_cast<const uint4*>(wrow + 16 * min(g + s, ksteps - 1));
-  };
-
   for (int i = wv; i < kProjRows; i += kProjWaves) {
     float* y = rows_s + i * ys;
     const int b = b0 + i;
     const bool last = i + kProjWaves >= kProjRows;
     if (b < a.batch) {
       merge_row<V, E, P, S>(a, b, h, lane, y);
-      if (active && last) load_w(kb);  // in flight during the rotation and the wait for the other rows
+      if (pw.active && last) pw.load_w(wf, pw.kb);  // in flight during the rotation and the wait for the other rows
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // this wave's LDS row is complete
       __builtin_amdgcn_wave_barrier();
       if (a.wht) rotate_row(y, y, a.d_latent, lane);
     } else {
-      if (active && last) load_w(kb);
+      if (pw.active && last) pw.load_w(wf, pw.kb);
       for (int j = lane; j < a.d_latent; j += 64) y[j] = 0.f;
     }
   }
   __syncthreads();
-
-  floatx16_t acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  if (active) {
-    const float* arow = rows_s + l32 * ys + 8 * half;  // A operand: lane l holds o[b0 + l % 32][16 s + 8 (l / 32) + i]
-    for (int g = kb; g < ke; g += 8) {
-      uint4 cur[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) cur[s] = wf[s];
-      if (g + 8 < ke) load_w(g + 8);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (g + s < ke) {
-          float x[8];
-          if (l32 < kProjRows) {
-            const float4 a0 = *reinterpret_cast<const float4*>(arow + 16 * (g + s));
-            const float4 a1 = *reinterpret_cast<const float4*>(arow + 16 * (g + s) + 4);
-            x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
-            x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = 0.f;
-          }
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hi[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-            const float r0 = x[2 * i] - bf16_to_f32(static_cast<uint16_t>(hi[i] & 0xffffu));
-            const float r1 = x[2 * i + 1] - bf16_to_f32(static_cast<uint16_t>(hi[i] >> 16));
-            lo[i] = pack_bf16x2(r0, r1);
-          }
-          const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, cur[s]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3])), bw, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), bw, acc, 0, 0, 0);
-        }
-      }
-    }
-  }
-  __syncthreads();  // every wave is done reading the rows
-  // Accumulator r of lane l is D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]: rows < kProjRows are
-  // r < kProjAcc, kProjAcc / 4 groups of four.
-  constexpr int NG = kProjAcc / 4;
-  floatx4_t* part = reinterpret_cast<floatx4_t*>(rows_s);  // [vp][kparts - 1][NG][64]
-  if (active && kq > 0) {
-#pragma unroll
-    for (int j = 0; j < NG; ++j)
-      part[((vt * (kparts - 1) + kq - 1) * NG + j) * 64 + lane] = floatx4_t{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
-  }
-  __syncthreads();
-  if (!active || kq > 0) return;
-  for (int q = 0; q < kparts - 1; ++q) {
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      const floatx4_t t = part[((vt * (kparts - 1) + q) * NG + j) * 64 + lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * j + e] += t[e];
-    }
-  }
-  const int vv = vt * 32 + l32;
-  if (vv >= p.d_v) return;
-#pragma unroll
-  for (int r = 0; r < kProjAcc; ++r) {
-    const int bb = b0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (bb < a.batch) p.out_v[(static_cast<int64_t>(bb) * a.heads + h) * p.d_v + vv] = acc[r];
-  }
+  const floatx16_t acc = proj_mfma(pw, rows_s, ys, wf, lane);
+  proj_reduce_store(pw, acc, rows_s, p, h, a.heads, b0, a.batch, lane);
 }
 
 // Context merge: decode results over P disjoint parts of every sequence's context combined by
@@ -625,22 +521,19 @@ hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream) {
 
 hipError_t launch_merge_project(const MergeLaunch& a, const uint16_t* w_uv, int d_v, float* out_v, int xcds,
                                 hipStream_t stream) {
-  if (a.d_latent > kMaxLatent || a.d_latent % 16 != 0 || d_v < 1 || d_v > 32 * kProjWaves || xcds < 1)
+  if (a.d_latent > kMaxLatent || a.d_latent % 16 != 0 || d_v < 1 || d_v > kProjMaxDv || xcds < 1)
     return hipErrorInvalidValue;
   if (a.wht && (a.d_latent & (a.d_latent - 1)) != 0) return hipErrorInvalidValue;
   ProjectArgs p;
   p.w = w_uv;
   p.d_v = d_v;
-  p.vp = 4;
-  while (p.vp * 32 < d_v) p.vp <<= 1;
+  p.vp = proj_vp(d_v);
   p.out_v = out_v;
   p.xcds = xcds;
   const int btiles = (a.batch + kProjRows - 1) / kProjRows;
   const int64_t blocks = static_cast<int64_t>((a.heads + xcds - 1) / xcds) * xcds * btiles;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int kparts = kProjWaves / p.vp;
-  const size_t lds = std::max<size_t>(static_cast<size_t>(kProjRows) * (a.d_latent + 4) * sizeof(float),
-                                      static_cast<size_t>(p.vp) * (kparts - 1) * (kProjAcc / 4) * 64 * sizeof(floatx4_t));
+  const size_t lds = proj_lds_bytes(a.d_latent, p.vp);
   // Sixteen waves per workgroup leave 128 registers per lane: the one-pass shapes holding 32 or
   // more float4 per lane (S E = 16) would spill, so they run with half the steps (sequences with
   // more partials than that take the general loop).

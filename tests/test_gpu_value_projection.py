@@ -16,10 +16,17 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
 # (name, batch, heads, d_latent, d_v, weight dtype): matrix-core tiles with whole and ragged
-# 32-row / 32-column blocks, a single element, and the fp32 path (fp32 weights, or a latent
-# width that is not a multiple of 16).
+# 32-row / 32-column blocks (batches of 32 and 64 at DeepSeek-V3 shapes; value widths up to 600;
+# latent widths up to 2064), a single element, and the fp32 path (fp32 weights, or a latent width
+# that is not a multiple of 16).
 SHAPES = [
     ("dsv3_shape", 32, 128, 512, 128, "bf16"),
+    ("paged_headline_batch", 64, 128, 512, 128, "bf16"),
+    ("two_kparts_dv256", 40, 4, 512, 256, "bf16"),
+    ("one_kpart_dv300", 19, 3, 256, 300, "bf16"),
+    ("latent_1024_lds_over_64k", 33, 2, 1024, 128, "bf16"),
+    ("dv600_tile_kernel", 5, 2, 128, 600, "bf16"),
+    ("latent_2064_tile_kernel", 3, 1, 2064, 64, "bf16"),
     ("ragged_rows_and_columns", 37, 3, 64, 45, "bf16"),
     ("one_output", 1, 1, 16, 1, "bf16"),
     ("two_row_blocks_g4_width", 70, 5, 128, 96, "bf16"),
