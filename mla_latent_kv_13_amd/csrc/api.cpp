@@ -337,14 +337,17 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
     L.seq_lens = row_len;
     L.row_seq = row_seq;
   }
-  if (plan.sched == 1) {
-    e = tpla::launch_tile_prefix(seq_lens, batch, reinterpret_cast<int*>(ws + plan.off_prefix), stream);
+  int* prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
+  if (plan.sched == 1 && !wht) {
+    e = tpla::launch_tile_prefix(seq_lens, batch, prefix, stream);
     if (e != hipSuccess) return hip_fail(e, "tile prefix launch");
   }
   if (wht) {
+    // the query rotation's launch also computes the tile prefix when the schedule needs one
     void* qrot = ws + plan.off_qrot;
     const int dst_f32 = plan.kernel == 1 ? 1 : 0;
-    e = tpla::launch_rotate_query(q_latent, d->dtype == TPLA_BF16 ? 1 : 0, batch * heads, d->d_latent, qrot, dst_f32, stream);
+    e = tpla::launch_rotate_query(q_latent, d->dtype == TPLA_BF16 ? 1 : 0, batch * heads, d->d_latent, qrot, dst_f32, stream,
+                                  seq_lens, batch, plan.sched == 1 ? prefix : nullptr);
     if (e != hipSuccess) return hip_fail(e, "query rotation launch");
     L.q_lat = qrot;
     L.q_lat_f32 = dst_f32;

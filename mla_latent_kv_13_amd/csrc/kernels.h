@@ -92,9 +92,12 @@ hipError_t launch_prefill_rows(const int* query_start, const int* seq_lens, int 
                                int max_seq_len, int* row_len, int* row_seq, hipStream_t stream);
 // Largest number of cache pages one segment of the MFMA kernel may span (its LDS page list).
 int mfma_max_segment_pages();
-// Rotate q_lat [B*H, d_c] by the Hadamard matrix into dst (fp32 if dst_f32, else bf16).
+// Rotate q_lat [B*H, d_c] by the Hadamard matrix into dst (fp32 if dst_f32, else bf16).  With
+// tile_prefix non-null the same launch also computes the tile prefix of seq_lens [batch] (as
+// launch_tile_prefix).
 hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_latent, void* dst, int dst_f32,
-                               hipStream_t stream);
+                               hipStream_t stream, const int* seq_lens = nullptr, int batch = 0,
+                               int* tile_prefix = nullptr);
 // norm_slices > 0: RMS-normalise the (rotated) latent over that many equal slices, unit gain.
 hipError_t launch_append(void* cache, const void* rows, const int64_t* slots, int64_t n, int d_latent, int d_rope,
                          int dtype, int wht, int norm_slices, float eps, hipStream_t stream);

@@ -402,10 +402,46 @@ __global__ __launch_bounds__(kThreads) void context_merge_kernel(ContextMergeLau
   }
 }
 
+// tile_prefix[b] = sum_{b' < b} ceil(seq_lens[b'] / 32) for b = 0..batch, by one whole block: each
+// thread sums a contiguous run of sequences, then an exclusive scan over the threads' sums.
+__device__ __forceinline__ void tile_prefix_block(const int* __restrict__ seq_lens, int batch, int* __restrict__ prefix) {
+  __shared__ int sums[kThreads];
+  const int per = (batch + kThreads - 1) / kThreads;
+  const int b0 = threadIdx.x * per, b1 = min(batch, b0 + per);
+  int own = 0;
+  for (int b = b0; b < b1; ++b) own += (seq_lens[b] + 31) >> 5;
+  sums[threadIdx.x] = own;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan (Hillis-Steele)
+    const int v = threadIdx.x >= off ? sums[threadIdx.x - off] : 0;
+    __syncthreads();
+    sums[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = sums[threadIdx.x] - own;  // exclusive
+  for (int b = b0; b < b1; ++b) {
+    prefix[b] = run;
+    run += (seq_lens[b] + 31) >> 5;
+  }
+  if (threadIdx.x == kThreads - 1) prefix[batch] = sums[kThreads - 1];
+}
+
+__global__ __launch_bounds__(kThreads) void tile_prefix_kernel(const int* __restrict__ seq_lens, int batch,
+                                                               int* __restrict__ prefix) {
+  tile_prefix_block(seq_lens, batch, prefix);
+}
+
 // One wave per query row, four rows per block: V consecutive values per lane, rotated in registers.
+// With a tile prefix to compute (prefix non-null) one more block, the last, computes it, so that a
+// call that needs both launches one kernel.
 template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void rotate_query_kernel(const T* __restrict__ q, int rows, int d_latent,
-                                                                 void* dst, int dst_f32) {
+                                                                 void* dst, int dst_f32, const int* __restrict__ seq_lens,
+                                                                 int batch, int* __restrict__ prefix) {
+  if (prefix != nullptr && blockIdx.x == gridDim.x - 1) {  // uniform over the block
+    tile_prefix_block(seq_lens, batch, prefix);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -430,42 +466,22 @@ __global__ __launch_bounds__(kThreads) void rotate_query_kernel(const T* __restr
 }
 
 template <typename T>
-hipError_t launch_rotate(const T* q, int rows, int d_latent, void* dst, int dst_f32, hipStream_t stream) {
-  const dim3 grid((rows + kMergeWaves - 1) / kMergeWaves);
+hipError_t launch_rotate(const T* q, int rows, int d_latent, void* dst, int dst_f32, const int* seq_lens, int batch,
+                         int* prefix, hipStream_t stream) {
+  const dim3 grid((rows + kMergeWaves - 1) / kMergeWaves + (prefix != nullptr ? 1 : 0));
+#define TPLA_ROT(VV)                                                                                            \
+  hipLaunchKernelGGL((rotate_query_kernel<T, VV>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32, \
+                     seq_lens, batch, prefix)
   switch (d_latent <= 64 ? 1 : d_latent / 64) {
-    case 1: hipLaunchKernelGGL((rotate_query_kernel<T, 1>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
-    case 2: hipLaunchKernelGGL((rotate_query_kernel<T, 2>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
-    case 4: hipLaunchKernelGGL((rotate_query_kernel<T, 4>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
-    case 8: hipLaunchKernelGGL((rotate_query_kernel<T, 8>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
-    case 16: hipLaunchKernelGGL((rotate_query_kernel<T, 16>), grid, dim3(kThreads), 0, stream, q, rows, d_latent, dst, dst_f32); break;
+    case 1: TPLA_ROT(1); break;
+    case 2: TPLA_ROT(2); break;
+    case 4: TPLA_ROT(4); break;
+    case 8: TPLA_ROT(8); break;
+    case 16: TPLA_ROT(16); break;
     default: return hipErrorInvalidValue;
   }
+#undef TPLA_ROT
   return hipGetLastError();
-}
-
-// tile_prefix[b] = sum_{b' < b} ceil(seq_lens[b'] / 32) for b = 0..batch, one block: each thread
-// sums a contiguous run of sequences, then an exclusive scan over the threads' sums.
-__global__ __launch_bounds__(kThreads) void tile_prefix_kernel(const int* __restrict__ seq_lens, int batch,
-                                                               int* __restrict__ prefix) {
-  __shared__ int sums[kThreads];
-  const int per = (batch + kThreads - 1) / kThreads;
-  const int b0 = threadIdx.x * per, b1 = min(batch, b0 + per);
-  int own = 0;
-  for (int b = b0; b < b1; ++b) own += (seq_lens[b] + 31) >> 5;
-  sums[threadIdx.x] = own;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan (Hillis-Steele)
-    const int v = threadIdx.x >= off ? sums[threadIdx.x - off] : 0;
-    __syncthreads();
-    sums[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int run = sums[threadIdx.x] - own;  // exclusive
-  for (int b = b0; b < b1; ++b) {
-    prefix[b] = run;
-    run += (seq_lens[b] + 31) >> 5;
-  }
-  if (threadIdx.x == kThreads - 1) prefix[batch] = sums[kThreads - 1];
 }
 
 // Merge kernel variants <V, E, P, S>, indexed by merge_variant().
@@ -589,10 +605,13 @@ hipError_t launch_context_merge(const ContextMergeLaunch& a, hipStream_t stream)
 }
 
 hipError_t launch_rotate_query(const void* q_lat, int dtype, int rows, int d_latent, void* dst, int dst_f32,
-                               hipStream_t stream) {
+                               hipStream_t stream, const int* seq_lens, int batch, int* tile_prefix) {
   if (d_latent > kMaxLatent || (d_latent & (d_latent - 1)) != 0) return hipErrorInvalidValue;
-  if (dtype == 0) return launch_rotate(static_cast<const float*>(q_lat), rows, d_latent, dst, dst_f32, stream);
-  return launch_rotate(static_cast<const uint16_t*>(q_lat), rows, d_latent, dst, dst_f32, stream);
+  if (dtype == 0)
+    return launch_rotate(static_cast<const float*>(q_lat), rows, d_latent, dst, dst_f32, seq_lens, batch, tile_prefix,
+                         stream);
+  return launch_rotate(static_cast<const uint16_t*>(q_lat), rows, d_latent, dst, dst_f32, seq_lens, batch, tile_prefix,
+                       stream);
 }
 
 }  // namespace tpla
