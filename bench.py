@@ -80,6 +80,9 @@ def parse():
                         "up-projection and the context merge")
     p.add_argument("--prefill-only", action="store_true",
                    help="only the absorbed MLA prefill step (4 sequences x 1024 new tokens of 4096 cached)")
+    p.add_argument("--projected-only", action="store_true",
+                   help="only the decode with the fused value up-projection against the two calls, on the "
+                        "workload --config names")
     p.add_argument("--calibration-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy three times (to scale HBM byte counters)")
     return p.parse_args()
@@ -813,6 +816,11 @@ def main():
 
     binding.load_library()
     torch.cuda.init()
+    if args.projected_only:
+        w = Workload(args.config, args.chunk_tokens, args.shard_count)
+        print(json.dumps({"projected_decode": time_projected(w, args.extra_steps, args.warmup, not args.no_flush)}),
+              flush=True)
+        return
     if args.prefill_only:
         print(json.dumps({"prefill": time_prefill(args.extra_steps, args.warmup, not args.no_flush)}), flush=True)
         return
