@@ -132,3 +132,39 @@ def test_fused_projection_errors():
                                               torch.zeros((4, 8, 40), dtype=torch.bfloat16, device="cuda:0"))
     assert e.value.status == 2  # d_latent not a multiple of 16
     torch.cuda.synchronize()
+
+
+def test_fused_projection_replays_from_a_hip_graph():
+    """The fused call (query rotation with the tile prefix, decode kernel, merge with the projection)
+    enqueues no memset, allocation or synchronisation, so it can be captured in a HIP graph: every
+    replay, with eager work and synchronisations between the replays, equals the eager call bit for bit."""
+    case = inputs.make_case(33, batch=20, heads=64, d_latent=512, d_rope=64, shards=2, len_range=(0, 900), paged=True,
+                            page_size=64, transform="wht", scale=1.0 / np.sqrt(192))
+    _, w = inputs.make_value_projection(34, batch=1, heads=64, d_latent=512, d_v=128)
+    dc = DeviceCase(case)
+    wt = to_torch(w, "bf16")
+
+    def call(**kw):
+        return binding.tpla_decode_sharded_projected(dc.desc, dc.pool, dc.block_table, dc.seq_lens, dc.q_lat, dc.q_rope,
+                                                     case.scale, case.shards, case.max_seq_len, wt, **kw)
+
+    eager_out, eager_lse = call()
+    out, lse = torch.empty_like(eager_out), torch.empty_like(eager_lse)
+    ws = binding.alloc_workspace(binding.workspace_size(dc.desc, case.batch, case.heads, 2, 2, case.max_seq_len),
+                                 "cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out_v=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out_v=out, lse=lse, workspace=ws)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out) and torch.equal(lse, eager_lse)
