@@ -16,7 +16,7 @@ TILE = 32
 
 
 def tile_prefix(seq_lens):
-    """tile_prefix[b] = tiles of sequences before b (tile_prefix_kernel)."""
+    """tile_prefix[b] = tiles of sequences before b (tile_prefix_block)."""
     tiles = (np.asarray(seq_lens, dtype=np.int64) + TILE - 1) // TILE
     return np.concatenate([[0], np.cumsum(tiles)])
 
