@@ -337,3 +337,21 @@ def test_balanced_workers_only_grow_past_the_staged_page_bound(lib):
     # decode of 64 sequences up to 131072 tokens (4096 tiles > 2041): shares must stay under the bound,
     # ceil(64 * 4096 / 2041) = 129 workers
     assert binding.workspace_size(g1, 64, heads, 1, 1, 131072) == _ru(65 * 4) + partials(64 + 129)
+
+
+def test_header_compiles_as_c99(tmp_path):
+    """include/tpla.h is a C interface: a C99 translation unit that includes it and takes the
+    address of every declared function compiles with gcc, warnings as errors."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    names = declared_functions()
+    src = tmp_path / "abi_check.c"
+    src.write_text('#include "tpla.h"\ntypedef void (*any_fn)(void);\nany_fn all_entry_points[] = {\n'
+                   + "".join(f"  (any_fn)&{n},\n" for n in names) + "};\n")
+    res = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                          "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
