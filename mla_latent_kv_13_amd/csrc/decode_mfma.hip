@@ -99,6 +99,24 @@ struct Cfg {
 
 __device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
 
+// Order of the MFMAs of one steady-state step of the one-wave-per-32-heads tiles: NQ logit
+// k-steps of the next tile (a dependent chain into one accumulator) spread evenly among NP value
+// steps of the current tile (independent: consecutive ones go to different column blocks).  A
+// dependent 32x32x16 MFMA cannot start until its predecessor's result is written back, which
+// takes about three times as long as the matrix core needs to accept an independent one, so the
+// value steps fill the gaps of the chain.  Op n is a value step when the running share of value
+// steps crosses an integer there; index(n) is its position among the ops of its kind.
+template <int NQ, int NP>
+struct Stream {
+  static constexpr int N = NQ + NP;
+  static constexpr bool pv(int n) { return ((n + 1) * NP) / N > (n * NP) / N; }
+  static constexpr int index(int n) {
+    int c = 0;
+    for (int m = 0; m < n; ++m) c += pv(m) == pv(n) ? 1 : 0;
+    return c;
+  }
+};
+
 template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
 __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decode_mfma_kernel(DecodeLaunch a, float scale_log2, int units,
                                                                        int members, int page_shift) {
@@ -375,7 +393,12 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     return alpha;
   };
   auto softmax_max = [&](const float (&x)[16], float& neg_m) { return max_final(fmaxf(max8(x, 0), max8(x, 8)), neg_m); };
-  // Second half, one pair of logits: p = 2^(cs*x - m_ref), packed to bf16 for the value product.
+  // A tile's maximum logit of the lane's head, scaled: over both lane halves (all 32 tokens).
+  auto tile_max = [&](const float (&x)[16]) {
+    const float rmax = fmaxf(max8(x, 0), max8(x, 8));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cs;
+  };  // Second half, one pair of logits: p = 2^(cs*x - m_ref), packed to bf16 for the value product.
   auto softmax_pair = [&](const float (&x)[16], int j, float neg_m, uint32_t (&pk)[8], float& ps) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m));
@@ -479,6 +502,99 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  // Two steady-state loops.  w = 128 (two waves per SIMD): one stream of MFMAs, the next tile's
+  // logits interleaved with this tile's value product, no per-tile maximum (weights are taken against
+  // the reference and their sum checked instead).  Other widths: the fenced loop below, which keeps
+  // the exponentials between the logit MFMAs and the next maximum between the value MFMAs.
+  constexpr bool STREAM = W == 128 && KS == 1;
+  if constexpr (STREAM) {
+    // Steady state, iteration i: tile i with tile i+1 resident.  Tile i's weights are taken first,
+    // against the reference m_ref, and their sum checked: every weight is at most the sum, so a
+    // sum above kOverflow (or not finite) means a logit more than log2(kOverflow) above m_ref,
+    // rare since m_ref starts at the segment's first tile's maximum; such a tile is refitted
+    // (m_ref raised to the tile's maximum, O and l rescaled, the weights taken again) before its
+    // value product.  Then one stream of MFMAs interleaves the logits of tile i+1 with tile i's
+    // value product (Stream above), each operand read out of LDS DQ steps ahead.
+    constexpr float kOverflow = 4096.0f;
+    constexpr int DQ = 4;
+    using S = Stream<KST, NV>;
+    int st_cur = 0, st_next = 1 % ST, st_issue = ST - 1;
+    float ps = 0.f;
+    uint32_t pk[8];
+    auto weights_of = [&](int valid) {
+      ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool k0 = 8 * ((2 * j) >> 2) + 4 * half + ((2 * j) & 3) < valid;
+        const bool k1 = 8 * ((2 * j + 1) >> 2) + 4 * half + ((2 * j + 1) & 3) < valid;
+        const float p0 = k0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m)) : 0.f;
+        const float p1 = k1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m)) : 0.f;
+        ps += p0 + p1;
+        pk[j] = pack_bf16x2(p0, p1);
+      }
+    };
+    auto refit = [&](int valid) {
+      const float m_new = fmaxf(m_ref, tile_max(x));
+      const float f = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      neg_m = -m_new;
+      l_run *= f;
+      rescale(f);
+      weights_of(valid);
+    };
+    for (int i = 0; i + 1 < n_tiles; ++i) {
+      wait_tile(min(n_tiles - 1, ST + i - 2) - (i + 1), std::integral_constant<int, ST - 3>{});
+      raw_barrier();  // tile i+1 visible; tile i-1's stage free
+      if (i + ST - 1 < n_tiles) issue(i + ST - 1, st_issue);
+      st_issue = st_issue + 1 == ST ? 0 : st_issue + 1;
+      const unsigned char* tn = tile_at(st_next);
+      const unsigned char* tc = tile_at(st_cur);
+      auto frag = [&](int n) -> uint4 {
+        if (S::pv(n)) return __builtin_bit_cast(uint4, vread(tc, S::index(n)));
+        return kread(tn, S::index(n));
+      };
+      uint4 fr[DQ];
+#pragma unroll
+      for (int n = 0; n < DQ; ++n)
+        if (n < S::N) fr[n] = frag(n);
+      weights_of(kNT);
+      if (__builtin_expect(__any(!(ps <= kOverflow)), 0)) refit(kNT);  // wave-uniform, rare
+      l_run += ps;
+      const uint4 pb[2] = {make_uint4(pk[0], pk[1], pk[2], pk[3]), make_uint4(pk[4], pk[5], pk[6], pk[7])};
+      __builtin_amdgcn_sched_barrier(0);
+      floatx16_t s_nxt;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s_nxt[j] = 0.f;
+#pragma unroll
+      for (int n = 0; n < S::N; ++n) {
+        if (S::pv(n)) {
+          const int v = S::index(n);
+          o_acc[v % C::CB] = mfma(fr[n % DQ], pb[v / C::CB], o_acc[v % C::CB]);
+        } else {
+          s_nxt = mfma(fr[n % DQ], qf[S::index(n)], s_nxt);
+        }
+        if (n + DQ < S::N) fr[n % DQ] = frag(n + DQ);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = s_nxt[j];
+      st_cur = st_next;
+      st_next = st_next + 1 == ST ? 0 : st_next + 1;
+    }
+    // Last tile (possibly partial): weights of the tokens past the end are exactly 0, also when
+    // the scale is zero; the same overflow check.
+    {
+      const int valid = t_end - (t_begin + (n_tiles - 1) * kNT);
+      weights_of(valid);
+      if (__any(!(ps <= kOverflow))) refit(valid);
+      l_run += ps;
+      const unsigned char* tile = tile_at(st_cur);
+      short8_t vf[NPV];
+#pragma unroll
+      for (int v = 0; v < NPV; ++v) vf[v] = vread(tile, v);
+      pv(tile, pk, vf);
+    }
+  } else {
   // Steady state, iteration i: tile i with tile i+1 resident.  Each k-step of the logits of tile
   // i+1 (one MFMA) also carries one read-ahead K fragment, up to one pair of tile i's softmax
   // weights and, in the last NPV steps, one value fragment of tile i; then comes tile i's value
@@ -558,6 +674,8 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
 #pragma unroll
     for (int v = 0; v < NPV; ++v) vf[v] = vread(tile, v);
     pv(tile, pk, vf);
+  }
+
   }
 
   // Chunk result: o = O / l, lse = ln 2 * (m + log2 l); the two lane halves hold disjoint tokens.
