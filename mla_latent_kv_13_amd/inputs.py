@@ -116,8 +116,8 @@ def make_case(seed: int, *, batch: int, heads: int, d_latent: int, d_rope: int, 
               lens=None, len_range=None, dtype: str = "bf16", scale: float | None = None,
               transform: str = "identity", paged: bool = False, page_size: int = 64,
               max_seq_len: int | None = None, extra_pages: int = 0,
-              channel_sigma: float | None = None, place_rows: bool = True,
-              name: str = "custom") -> Case:
+              channel_sigma: float | None = None, token_gain: float | None = None,
+              place_rows: bool = True, name: str = "custom") -> Case:
     """Build a seeded case.
 
     ``lens`` gives the context length of every sequence (int or list);
@@ -126,6 +126,10 @@ def make_case(seed: int, *, batch: int, heads: int, d_latent: int, d_rope: int, 
     ``max_seq_len`` rows and no block table.  A paged layout uses
     ``page_size``-row pages, assigned by a seeded random permutation, plus
     ``extra_pages`` NaN-filled pages that no sequence uses.
+    ``token_gain`` scales the rows of each sequence geometrically along its
+    tokens, from 1 at the first token to ``token_gain`` at the last (before the
+    rounding to the stored dtype), so that later tiles hold much larger logits
+    than the first: a decode then has to raise its running maximum mid-sequence.
     """
     if lens is not None:
         seq_lens = np.broadcast_to(np.asarray(lens, dtype=np.int64), (batch,)).astype(np.int32).copy()
@@ -159,6 +163,9 @@ def make_case(seed: int, *, batch: int, heads: int, d_latent: int, d_rope: int, 
             lat = lat * chan[None, :]
         rows32[off:off + t_b, :d_latent] = lat
         rows32[off:off + t_b, d_latent:] = rng_rope.standard_normal((t_b, d_rope), dtype=np.float32)
+        if token_gain is not None and t_b > 1:
+            ramp = np.float32(token_gain) ** (np.arange(t_b, dtype=np.float32) / np.float32(t_b - 1))
+            rows32[off:off + t_b] *= ramp[:, None]
         off += t_b
     rows = _to_dtype(rows32, dtype)
     del rows32
@@ -194,7 +201,7 @@ def make_case(seed: int, *, batch: int, heads: int, d_latent: int, d_rope: int, 
                 shards=shards, scale=scale, transform=transform, page_size=psize, num_pages=num_pages,
                 max_seq_len=max_seq_len, paged=paged, q_lat=q_lat, q_rope=q_rope, seq_lens=seq_lens,
                 block_table=block_table, rows=rows, slots=slots,
-                meta=dict(seed=seed, channel_sigma=channel_sigma, extra_pages=extra_pages))
+                meta=dict(seed=seed, channel_sigma=channel_sigma, token_gain=token_gain, extra_pages=extra_pages))
     if place_rows:
         pool = case.empty_pool()
         pool.reshape(num_pages * psize, width)[slots] = rows

@@ -58,6 +58,18 @@ SMALL = [
                                  paged=True, page_size=32), {}),
     ("f32_wht_dl32", dict(batch=2, heads=3, d_latent=32, d_rope=8, shards=2, lens=[40, 7], dtype="f32",
                           transform="wht"), {}),
+    # Rows growing 8-fold along each sequence: later tiles' logits exceed the first tile's maximum
+    # by 12-26 (base 2), so the running maximum is raised mid-segment (O and l rescaled) on every
+    # tile width, and the 128-wide slices refit tiles whose weights would overflow
+    ("g4_h64_rising_logits", dict(batch=2, heads=64, shards=4, lens=[1500, 300], token_gain=8.0), {}),
+    ("g4_h128_rising_logits_balanced", dict(batch=3, heads=128, shards=4, lens=[900, 40, 2100], token_gain=8.0),
+     dict(schedule="balanced")),
+    ("g2_h128_rising_logits_paged_wht", dict(batch=2, heads=128, shards=2, lens=[2000, 200], paged=True, page_size=64,
+                                             transform="wht", token_gain=8.0), {}),
+    ("g1_h128_rising_logits", dict(batch=2, heads=128, shards=1, lens=[1200, 90], token_gain=8.0),
+     dict(chunk_tokens=512)),
+    ("g2_h32_rising_logits_generic", dict(batch=2, heads=32, shards=2, lens=[700, 64], token_gain=8.0),
+     dict(kernel="generic")),
 ]
 
 

@@ -68,3 +68,19 @@ def test_prefill_queries_layout_and_determinism():
     assert f32[1].dtype == np.float32 and np.isfinite(f32[1]).all()
     none = inputs.make_prefill_queries(1, new_tokens=[0, 0], heads=2, d_latent=8, d_rope=8)
     assert list(none[0]) == [0, 0, 0] and none[1].shape == (0, 2, 8)
+
+
+def test_token_gain_scales_rows_along_each_sequence():
+    """The same draws as without the gain, row t of a T-token sequence times gain ** (t / (T - 1));
+    one-token sequences are left as drawn."""
+    kw = dict(batch=3, heads=4, d_latent=64, d_rope=16, shards=2, lens=[100, 1, 33], dtype="f32")
+    plain = inputs.make_case(11, **kw)
+    grown = inputs.make_case(11, token_gain=8.0, **kw)
+    off = 0
+    for t_b in plain.seq_lens:
+        t_b = int(t_b)
+        a, g = plain.rows[off:off + t_b], grown.rows[off:off + t_b]
+        ramp = 8.0 ** (np.arange(t_b) / max(t_b - 1, 1)) if t_b > 1 else np.ones(1)
+        np.testing.assert_allclose(g, a * ramp[:, None], rtol=1e-6)
+        off += t_b
+    assert np.array_equal(plain.q_lat, grown.q_lat) and np.array_equal(plain.slots, grown.slots)
