@@ -387,7 +387,8 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     const float tmax = rmax * cs;
     const float m_new = tmax > m_ref + 8.0f ? tmax : m_ref;      // first tile: m_ref = -inf
-    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // exactly 1 when not raised, 0 first
+    float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);         // exactly 1 when not raised, 0 first
+    asm volatile("" : "+v"(alpha));  // computed here, in a value step, not sunk to the loop's end
     m_ref = m_new;
     neg_m = -m_new;
     return alpha;
@@ -398,11 +399,16 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     const float rmax = fmaxf(max8(x, 0), max8(x, 8));
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cs;
-  };  // Second half, one pair of logits: p = 2^(cs*x - m_ref), packed to bf16 for the value product.
+  };
+  // Second half, one pair of logits: p = 2^(cs*x - m_ref), packed to bf16 for the value product,
+  // and added to the running sum ps (started by pair 0).  The empty asm holds each addition in the
+  // step that computes its pair: otherwise the compiler sinks the whole dependent chain of
+  // additions to the end of the iteration, after the last value MFMA and before the next barrier.
   auto softmax_pair = [&](const float (&x)[16], int j, float neg_m, uint32_t (&pk)[8], float& ps) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m));
-    ps += p0 + p1;
+    ps = j == 0 ? p0 + p1 : ps + (p0 + p1);
+    asm volatile("" : "+v"(ps));
     pk[j] = pack_bf16x2(p0, p1);
   };
   auto rescale = [&](float alpha) {
