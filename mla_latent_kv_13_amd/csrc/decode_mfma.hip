@@ -528,14 +528,13 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     float ps = 0.f;
     uint32_t pk[8];
     auto weights_of = [&](int valid) {
-      ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const bool k0 = 8 * ((2 * j) >> 2) + 4 * half + ((2 * j) & 3) < valid;
         const bool k1 = 8 * ((2 * j + 1) >> 2) + 4 * half + ((2 * j + 1) & 3) < valid;
         const float p0 = k0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m)) : 0.f;
         const float p1 = k1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m)) : 0.f;
-        ps += p0 + p1;
+        ps = j == 0 ? p0 + p1 : ps + (p0 + p1);  // weights are >= +0: the same sum as from 0
         pk[j] = pack_bf16x2(p0, p1);
       }
     };
@@ -671,7 +670,7 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
       const bool k1 = 8 * ((2 * j + 1) >> 2) + 4 * half + ((2 * j + 1) & 3) < valid;
       const float p0 = k0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m)) : 0.f;
       const float p1 = k1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m)) : 0.f;
-      ps += p0 + p1;
+      ps = j == 0 ? p0 + p1 : ps + (p0 + p1);
       pk[j] = pack_bf16x2(p0, p1);
     }
     l_run = __builtin_fmaf(l_run, alpha, ps);
