@@ -70,6 +70,14 @@ SMALL = [
      dict(chunk_tokens=512)),
     ("g2_h32_rising_logits_generic", dict(batch=2, heads=32, shards=2, lens=[700, 64], token_gain=8.0),
      dict(kernel="generic")),
+    # page sizes that are not powers of two: page and offset of a token by division, on every kernel
+    ("g2_h128_paged48", dict(batch=3, heads=128, shards=2, lens=[700, 47, 1000], paged=True, page_size=48), {}),
+    ("g4_h64_paged96_balanced", dict(batch=3, heads=64, shards=4, lens=[500, 96, 1], paged=True, page_size=96),
+     dict(schedule="balanced")),
+    ("g1_h128_paged100_wht", dict(batch=2, heads=128, shards=1, lens=[640, 99], paged=True, page_size=100,
+                                  transform="wht"), {}),
+    ("f32_g2_paged24_generic", dict(batch=2, heads=4, d_latent=64, d_rope=16, shards=2, lens=[100, 23], dtype="f32",
+                                    paged=True, page_size=24), {}),
 ]
 
 
