@@ -350,16 +350,27 @@ __global__ __launch_bounds__(kThreads) void context_merge_kernel(ContextMergeLau
   };
   load(0);
   float m = -INFINITY;
-  for (int p0 = 0; p0 < a.parts; p0 += PB) {
-    float l[PB];
-#pragma unroll
-    for (int k = 0; k < PB; ++k) l[k] = a.lse_parts[min(p0 + k, a.parts - 1) * lse_stride + lse_at];
-#pragma unroll
-    for (int k = 0; k < PB; ++k) m = fmaxf(m, l[k]);  // a repeated last part does not change the maximum
-  }
   float z = 0.f;
-  if (m != -INFINITY)
-    for (int p = 0; p < a.parts; ++p) z += expf(a.lse_parts[p * lse_stride + lse_at] - m);
+  if (a.parts <= PB) {
+    // every part's log-sum-exp arrived with the first load: no further round trip to memory
+#pragma unroll
+    for (int k = 0; k < PB; ++k) m = fmaxf(m, lp[k]);  // a repeated last part does not change the maximum
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < PB; ++k)
+        if (k < a.parts) z += expf(lp[k] - m);
+    }
+  } else {
+    for (int p0 = 0; p0 < a.parts; p0 += PB) {
+      float l[PB];
+#pragma unroll
+      for (int k = 0; k < PB; ++k) l[k] = a.lse_parts[min(p0 + k, a.parts - 1) * lse_stride + lse_at];
+#pragma unroll
+      for (int k = 0; k < PB; ++k) m = fmaxf(m, l[k]);
+    }
+    if (m != -INFINITY)
+      for (int p = 0; p < a.parts; ++p) z += expf(a.lse_parts[p * lse_stride + lse_at] - m);
+  }
   const float lse_i = m != -INFINITY ? m + logf(z) : -INFINITY;
   if (a.lse != nullptr && mine) a.lse[lse_at] = lse_i;
 
@@ -438,12 +449,15 @@ template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void rotate_query_kernel(const T* __restrict__ q, int rows, int d_latent,
                                                                  void* dst, int dst_f32, const int* __restrict__ seq_lens,
                                                                  int batch, int* __restrict__ prefix) {
-  if (prefix != nullptr && blockIdx.x == gridDim.x - 1) {  // uniform over the block
+  // With a prefix to compute, block 0 computes it (dispatched first, so that it runs beside the
+  // rotation rather than after it) and the rows start at block 1.
+  const int blk = static_cast<int>(blockIdx.x) - (prefix != nullptr ? 1 : 0);
+  if (blk < 0) {  // uniform over the block
     tile_prefix_block(seq_lens, batch, prefix);
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
+  const int64_t r = static_cast<int64_t>(blk) * kMergeWaves + (threadIdx.x >> 6);
   if (r >= rows) return;
   const bool on = lane < d_latent / V;
   const Pack<T, V> p = on ? reinterpret_cast<const Pack<T, V>*>(q + r * d_latent)[lane] : Pack<T, V>{};
