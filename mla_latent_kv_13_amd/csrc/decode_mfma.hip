@@ -267,6 +267,12 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     }
   };
 
+  // The k-step of the key width that this wave's k-th step covers.  KS = 2: the waves of a pair
+  // take alternate pairs of k-steps (wave kh the steps 4j + 2kh and 4j + 2kh + 1), so that within
+  // a wave the LDS offsets of the K operand differ by compile-time amounts (see koff).
+  auto kstep = [&](int k) { return KS == 1 ? k : 4 * (k >> 1) + 2 * kh + (k & 1); };
+  static_assert(KS == 1 || (C::KW / 16) % 4 == 0, "whole groups of four k-steps per pair");
+
   // Q^T operand of this wave's k-steps: lane holds features 16*kk + 8*half .. +7 of its head.
   uint4 qf[C::KSTEPS];
   {
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     const uint16_t* qr = static_cast<const uint16_t*>(a.q_rope) + (static_cast<int64_t>(b) * a.heads + head) * DR;
 #pragma unroll
     for (int k = 0; k < C::KSTEPS; ++k) {
-      const int f = 16 * (kh * C::KSTEPS + k) + 8 * half;
+      const int f = 16 * kstep(k) + 8 * half;
       qf[k] = (f < W) ? *reinterpret_cast<const uint4*>(ql + f) : *reinterpret_cast<const uint4*>(qr + (f - W));
     }
   }
@@ -299,9 +305,14 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
 
   // Per-lane LDS offsets (bytes) of the swizzled operand reads.
   const int swk = swz(l32);  // K operand: token l32
+  // koff[m]: k-steps kk with kk % 4 = m (KS = 1), or with kk % 4 = 2 kh + m (KS = 2, m < 2); the
+  // rest of a step's offset, 128 bytes per group of four k-steps, is a compile-time constant.
   int koff[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) koff[m] = l32 * C::ROW_BYTES + ((((2 * m) | half) ^ swk) << 4);
+  for (int m = 0; m < 4; ++m) {
+    const int mm = KS == 1 ? m : 2 * kh + (m & 1);
+    koff[m] = l32 * C::ROW_BYTES + ((((2 * mm) | half) ^ swk) << 4);
+  }
   const int grp = lane >> 4, q = lane & 15;
   const int vt = 4 * half + (q >> 2);  // V operand: token vt (low read) and vt + 8 (high read) of a 16-token step
   int voff[2][2];
@@ -335,8 +346,8 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
 
   auto tile_at = [&](int stage) { return lds + stage * C::TILE_BYTES; };
   auto kread = [&](const unsigned char* tile, int k) {
-    const int kk = kh * KST + k;
-    return *reinterpret_cast<const uint4*>(tile + koff[kk & 3] + ((kk >> 2) << 7));
+    if constexpr (KS == 1) return *reinterpret_cast<const uint4*>(tile + koff[k & 3] + ((k >> 2) << 7));
+    return *reinterpret_cast<const uint4*>(tile + koff[k & 1] + ((k >> 1) << 7));
   };
   // Value fragment v = ks * CB + cbl: tokens 16*ks.., value block kh*CB + cbl.
   auto vread = [&](const unsigned char* tile, int v) {
