@@ -222,6 +222,12 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   }
   // Byte address of cache row `row`.
   auto row_addr = [&](int64_t row) { return cache + row * D * 2; };
+  // Full tiles of layouts 0 and 1 address their first row in 32 x 32 -> 64-bit scalar products:
+  // layout 0 from the sequence's first row (once per segment), layout 1 from its page (the host
+  // takes layout 1 only when a page's bytes fit 32 bits).
+  const uint32_t row_bytes = static_cast<uint32_t>(D * 2);
+  const uint32_t page_bytes = static_cast<uint32_t>(page_size) * row_bytes;
+  const unsigned char* seq_rows = LAYOUT == 0 ? cache + static_cast<int64_t>(bs) * page_size * (D * 2) : cache;
   auto row_of = [&](int t) -> int64_t {
     if constexpr (LAYOUT == 0) {
       return static_cast<int64_t>(bs) * page_size + t;
@@ -242,11 +248,10 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
       if constexpr (LAYOUT == 1) {
         // power-of-two pages of at least 32 rows: the tile sits in one page; its address is
         // formed in scalar registers from the page number
-        const int pg = __builtin_amdgcn_readfirstlane(pages[(t0 >> page_shift) - first_page]);
-        const int64_t row = (static_cast<int64_t>(pg) << page_shift) + (t0 & (page_size - 1));
-        base = cache + row * (D * 2);
+        const uint32_t pg = __builtin_amdgcn_readfirstlane(pages[(t0 >> page_shift) - first_page]);
+        base = cache + static_cast<uint64_t>(pg) * page_bytes + static_cast<uint32_t>(t0 & (page_size - 1)) * row_bytes;
       } else {
-        base = uniform_ptr(row_addr(row_of(t0)));
+        base = uniform_ptr(seq_rows + static_cast<uint64_t>(static_cast<uint32_t>(t0)) * row_bytes);
       }
 #pragma unroll
       for (int k = 0; k < C::PER_MAX; ++k) {
@@ -738,7 +743,10 @@ hipError_t launch_one(const DecodeLaunch& a, hipStream_t stream) {
 template <int W, int DR, int HB, int KS, int STQ>
 hipError_t launch_layout(const DecodeLaunch& a, hipStream_t stream) {
   if (a.block_table == nullptr) return launch_one<W, DR, HB, KS, STQ, 0>(a, stream);
-  if (a.page_size % kNT == 0 && (a.page_size & (a.page_size - 1)) == 0) return launch_one<W, DR, HB, KS, STQ, 1>(a, stream);
+  // layout 1: power-of-two pages of whole tiles whose bytes fit 32 bits (the kernel's page address)
+  const bool page_fits = static_cast<int64_t>(a.page_size) * (a.d_latent + DR) * 2 < (int64_t{1} << 32);
+  if (a.page_size % kNT == 0 && (a.page_size & (a.page_size - 1)) == 0 && page_fits)
+    return launch_one<W, DR, HB, KS, STQ, 1>(a, stream);
   return launch_one<W, DR, HB, KS, STQ, 2>(a, stream);
 }
 
