@@ -416,16 +416,21 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cs;
   };
-  // Second half, one pair of logits: p = 2^(cs*x - m_ref), packed to bf16 for the value product,
-  // and added to the running sum ps (started by pair 0).  The empty asm holds each addition in the
-  // step that computes its pair: otherwise the compiler sinks the whole dependent chain of
-  // additions to the end of the iteration, after the last value MFMA and before the next barrier.
-  auto softmax_pair = [&](const float (&x)[16], int j, float neg_m, uint32_t (&pk)[8], float& ps) {
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j], cs, neg_m));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j + 1], cs, neg_m));
-    ps = j == 0 ? p0 + p1 : ps + (p0 + p1);
+  // Second half of the online softmax, one logit e (0..15) at a time: p = 2^(cs*x - m_ref), packed
+  // to bf16 by pairs for the value product and added to the running sum ps by pairs (started by
+  // pair 0); the first of a pair waits in p_lo.  One exponential per logit step, so that each
+  // hides under its step's MFMA.  The empty asm holds each addition in the step that computes
+  // its pair: otherwise the compiler sinks the whole dependent chain of additions to the end of
+  // the iteration, after the last value MFMA and before the next barrier.
+  auto softmax_one = [&](const float (&x)[16], int e, float neg_m, uint32_t (&pk)[8], float& p_lo, float& ps) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], cs, neg_m));
+    if ((e & 1) == 0) {
+      p_lo = p;
+      return;
+    }
+    ps = e == 1 ? p_lo + p : ps + (p_lo + p);
     asm volatile("" : "+v"(ps));
-    pk[j] = pack_bf16x2(p0, p1);
+    pk[e >> 1] = pack_bf16x2(p_lo, p);
   };
   auto rescale = [&](float alpha) {
 #pragma unroll
@@ -617,8 +622,8 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     }
   } else {
   // Steady state, iteration i: tile i with tile i+1 resident.  Each k-step of the logits of tile
-  // i+1 (one MFMA) also carries one read-ahead K fragment, up to one pair of tile i's softmax
-  // weights and, in the last NPV steps, one value fragment of tile i; then comes tile i's value
+  // i+1 (one MFMA) also carries one read-ahead K fragment, up to one of tile i's softmax weights
+  // and, in the last NPV steps, one value fragment of tile i; then comes tile i's value
   // product, whose steps carry the maximum of tile i+1 (with the pair's exchange at KS = 2).  The
   // steps are fenced so that the compiler keeps this order, which hides the LDS latency behind
   // the matrix cores and the softmax arithmetic in the gaps between MFMA issues.
@@ -645,15 +650,15 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
       floatx16_t s_nxt;
 #pragma unroll
       for (int j = 0; j < 16; ++j) s_nxt[j] = 0.f;
-      float ps = 0.f;
+      float ps = 0.f, p_lo = 0.f;
       short8_t vf[NPV];
 #pragma unroll
       for (int k = 0; k < KST; ++k) {
         s_nxt = mfma(kf[k % NPF], qf[k], s_nxt);
         if (k + NPF < KST) kf[k % NPF] = kread(tn, k + NPF);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if ((j * KST) / 8 == k) softmax_pair(x, j, neg_m, pk, ps);
+        for (int e = 0; e < 16; ++e)
+          if ((e * KST) / 16 == k) softmax_one(x, e, neg_m, pk, p_lo, ps);
         if (k >= KST - NPV) vf[k - (KST - NPV)] = vread(tc, k - (KST - NPV));
         __builtin_amdgcn_sched_barrier(0);
       }
