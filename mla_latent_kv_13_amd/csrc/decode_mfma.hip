@@ -249,7 +249,8 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
         // power-of-two pages of at least 32 rows: the tile sits in one page; its address is
         // formed in scalar registers from the page number
         const uint32_t pg = __builtin_amdgcn_readfirstlane(pages[(t0 >> page_shift) - first_page]);
-        base = cache + static_cast<uint64_t>(pg) * page_bytes + static_cast<uint32_t>(t0 & (page_size - 1)) * row_bytes;
+        base = uniform_ptr(cache + static_cast<uint64_t>(pg) * page_bytes +
+                           static_cast<uint32_t>(t0 & (page_size - 1)) * row_bytes);
       } else {
         base = uniform_ptr(seq_rows + static_cast<uint64_t>(static_cast<uint32_t>(t0)) * row_bytes);
       }
@@ -422,15 +423,21 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   // hides under its step's MFMA.  The empty asm holds each addition in the step that computes
   // its pair: otherwise the compiler sinks the whole dependent chain of additions to the end of
   // the iteration, after the last value MFMA and before the next barrier.
-  auto softmax_one = [&](const float (&x)[16], int e, float neg_m, uint32_t (&pk)[8], float& p_lo, float& ps) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], cs, neg_m));
-    if ((e & 1) == 0) {
-      p_lo = p;
-      return;
-    }
-    ps = e == 1 ? p_lo + p : ps + (p_lo + p);
+  // KS = 1: a pair is summed and packed one step after its second exponential, so that the
+  // exponential's latency passes under that step's MFMA (the last pair after the loop); at KS = 2
+  // finishing a pair in its own step measured faster.
+  constexpr bool DEFER = KS == 1;
+  auto finish_pair = [&](int j, float p0, float p1, uint32_t (&pk)[8], float& ps) {
+    ps = j == 0 ? p0 + p1 : ps + (p0 + p1);
     asm volatile("" : "+v"(ps));
-    pk[e >> 1] = pack_bf16x2(p_lo, p);
+    pk[j] = pack_bf16x2(p0, p1);
+  };
+  auto softmax_one = [&](const float (&x)[16], int e, float neg_m, uint32_t (&pk)[8], float& p_lo, float& p_hi,
+                         float& ps) {
+    if (DEFER && (e & 1) == 0 && e > 0) finish_pair((e >> 1) - 1, p_lo, p_hi, pk, ps);
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], cs, neg_m));
+    if ((e & 1) == 0) p_lo = p; else p_hi = p;
+    if (!DEFER && (e & 1) == 1) finish_pair(e >> 1, p_lo, p_hi, pk, ps);
   };
   auto rescale = [&](float alpha) {
 #pragma unroll
@@ -650,7 +657,7 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
       floatx16_t s_nxt;
 #pragma unroll
       for (int j = 0; j < 16; ++j) s_nxt[j] = 0.f;
-      float ps = 0.f, p_lo = 0.f;
+      float ps = 0.f, p_lo = 0.f, p_hi = 0.f;
       short8_t vf[NPV];
 #pragma unroll
       for (int k = 0; k < KST; ++k) {
@@ -658,10 +665,11 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
         if (k + NPF < KST) kf[k % NPF] = kread(tn, k + NPF);
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if ((e * KST) / 16 == k) softmax_one(x, e, neg_m, pk, p_lo, ps);
+          if ((e * KST) / 16 == k) softmax_one(x, e, neg_m, pk, p_lo, p_hi, ps);
         if (k >= KST - NPV) vf[k - (KST - NPV)] = vread(tc, k - (KST - NPV));
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (DEFER) finish_pair(7, p_lo, p_hi, pk, ps);
       l_run = __builtin_fmaf(l_run, alpha, ps);
       if constexpr (KS > 1) sx_write(s_nxt);
       const float m_old = m_ref;
