@@ -66,7 +66,8 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=30, help="untimed steps first (the first 10-20 calls of a process run ~2%% slow)")
+    p.add_argument("--warmup", type=int, default=60,
+                   help="untimed steps first (a process's decode kernels run slower over its first ~50 calls as the card settles)")
     p.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5], help="headline workload")
     p.add_argument("--shard-count", type=int, default=0,
                    help="headline call computes shards [0, n) only (0 = all): n = 1 is one device's share")
