@@ -769,10 +769,10 @@ hipError_t launch_layout(const DecodeLaunch& a, hipStream_t stream) {
 #define TPLA_W128_CFG 4, 1, 6
 #endif
 #ifndef TPLA_W256_CFG
-#define TPLA_W256_CFG 4, 1, 6
+#define TPLA_W256_CFG 4, 1, 5
 #endif
 #ifndef TPLA_W512_CFG
-#define TPLA_W512_CFG 2, 2, 4
+#define TPLA_W512_CFG 2, 2, 3
 #endif
 struct TileCfg {
   int hb_max, ks, st;
