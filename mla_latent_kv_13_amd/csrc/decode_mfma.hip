@@ -240,7 +240,8 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   };
 
   auto issue = [&](int j, int stage) {
-    const int t0 = t_begin + j * kNT;
+    // wave-uniform; taken as such so that the tile's address arithmetic stays on the scalar unit
+    const int t0 = __builtin_amdgcn_readfirstlane(t_begin + j * kNT);
     const uint32_t dst = lds_base + stage * C::TILE_BYTES;
     if (LAYOUT != 2 && t0 + kNT <= t_end) {
       // 32 consecutive rows: one uniform base, per-lane constant offsets
