@@ -326,6 +326,9 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
   L.tile_prefix = reinterpret_cast<const int*>(ws + plan.off_prefix);
   L.row_seq = nullptr;
   L.xcds = device_shape().xcds;
+  L.direct_out = nullptr;
+  L.direct_lse = nullptr;
+  L.direct_wht = wht ? 1 : 0;
 
   hipError_t e;
   if (pf) {
@@ -336,6 +339,12 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
     seq_lens = row_len;  // from here on every row is a decode row over its own prefix
     L.seq_lens = row_len;
     L.row_seq = row_seq;
+    // exact MLA over the whole latent under the balanced schedule: a row that one worker
+    // computes whole (most prefill rows) is finished in the decode kernel, not merged
+    if (plan.kernel == 2 && plan.sched == 1 && num_shards == 1 && shard_count == 1 && tpla::mfma_direct_rows(w)) {
+      L.direct_out = out;
+      L.direct_lse = lse;
+    }
   }
   int* prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
   if (plan.sched == 1 && !wht) {
@@ -385,6 +394,7 @@ int32_t decode_impl(const tpla_cache_desc_t* d, const void* cache, const int32_t
   M.wht = wht ? 1 : 0;
   M.out = out;
   M.lse = lse;
+  M.skip_whole = L.direct_out != nullptr ? 1 : 0;
   if (proj) {
     e = tpla::launch_merge_project(M, static_cast<const uint16_t*>(proj->w_uv), proj->d_v, proj->out_v,
                                    device_shape().xcds, stream);

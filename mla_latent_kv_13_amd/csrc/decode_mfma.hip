@@ -117,7 +117,113 @@ struct Stream {
   }
 };
 
-template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
+// Tiles that finish whole rows themselves (DecodeLaunch::direct_out): the full 512-wide latent
+// of one shard split between the two waves of a pair, 256 value columns each.
+constexpr bool direct_rows(int w, int ks) { return w == 512 && ks == 2; }
+
+// H2 butterfly on one index bit: the lower index takes the sum, the upper the difference.
+__device__ __forceinline__ void bfly(float& lo, float& hi) {
+  const float u = lo, v = hi;
+  lo = u + v;
+  hi = u - v;
+}
+
+// Butterflies on index bit K of N registers (every index a compile-time constant, so that the
+// array stays in registers).
+template <int K, int N>
+__device__ __forceinline__ void bfly_bit(float (&z)[N]) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const int r = ((i >> K) << (K + 1)) | (i & ((1 << K) - 1));
+    bfly(z[r], z[r | (1 << K)]);
+  }
+}
+
+// Final output of a row that one workgroup computed whole, from one wave of a pair: this wave's
+// O^T accumulators (CB = 8 blocks of 32 columns, kh * 256 + 32 * cb + 8 * (j / 4) + 4 * half +
+// j % 4 for accumulator j, head = lane % 32) are normalised, rotated back by the orthonormal
+// Sylvester Hadamard matrix when the cache is rotated (out = H y, the merge's definition), and
+// written with the log-sum-exp.  H is the product of one 2-point butterfly per bit of the column
+// index: the accumulator-index bits are butterflied in registers, the lane-half bit across the
+// two halves of the wave (permlane32 swaps), and the wave bit through LDS: wave kh = 0 finishes
+// columns c and c + 256 for c in [0, 128), wave kh = 1 for c in [128, 256), each sending the other
+// the half of its values it does not finish (16 KiB per wave at `mine`, read back at `theirs`).
+template <int CB>
+__device__ __forceinline__ void finish_row(const floatx16_t (&o_acc)[CB], float l_tot, float m_ref, const DecodeLaunch& a,
+                                           int b, int head, int kh, int half, int lane, unsigned char* mine,
+                                           const unsigned char* theirs) {
+  static_assert(CB == 8, "a pair of 256-column halves");
+  float z[CB * 16];  // z[16 * cb + j]
+  const float f = (a.direct_wht ? 0.044194173824159216f : 1.0f) / l_tot;  // 1/sqrt(512) with H
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z[16 * cb + j] = o_acc[cb][j] * f;
+  float* out = a.direct_out + (static_cast<int64_t>(b) * a.heads + head) * 512;
+  if (!a.direct_wht) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        *reinterpret_cast<float4*>(out + kh * 256 + 32 * cb + 8 * j4 + 4 * half) =
+            make_float4(z[16 * cb + 4 * j4], z[16 * cb + 4 * j4 + 1], z[16 * cb + 4 * j4 + 2], z[16 * cb + 4 * j4 + 3]);
+  } else {
+    // register bits: z index bits 0-1 = column bits 0-1, bits 2-3 = column bits 3-4, bits 4-6 =
+    // column bits 5-7 (the lower column always has the lower index)
+    bfly_bit<0>(z);
+    bfly_bit<1>(z);
+    bfly_bit<2>(z);
+    bfly_bit<3>(z);
+    bfly_bit<4>(z);
+    bfly_bit<5>(z);
+    bfly_bit<6>(z);
+    // lane-half bit (column bit 2): swap halves between register pairs, butterfly in the lane,
+    // swap back.  After the first swap a lane below 32 holds both halves of z[r], a lane above 32
+    // both halves of z[r + 1].
+#pragma unroll
+    for (int r = 0; r < CB * 16; r += 2) {
+      const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[r]), __float_as_uint(z[r + 1]), false, false);
+      float lo = __uint_as_float(s1[0]), hi = __uint_as_float(s1[1]);
+      bfly(lo, hi);
+      const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+      z[r] = __uint_as_float(s2[0]);
+      z[r + 1] = __uint_as_float(s2[1]);
+    }
+    // wave bit (column bit 8): blocks cb = 4 .. 7 (kh = 0) or 0 .. 3 (kh = 1) go to the partner
+    // (selected per value, so that every register index stays a constant)
+    const bool k0 = kh == 0;
+    __syncthreads();  // every wave is done with the ring, which now holds the exchange
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float g[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[e] = k0 ? z[64 + 4 * i + e] : z[4 * i + e];
+      reinterpret_cast<float4*>(mine)[i * 64 + lane] = make_float4(g[0], g[1], g[2], g[3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 t = reinterpret_cast<const float4*>(theirs)[i * 64 + lane];
+      const float o4[4] = {t.x, t.y, t.z, t.w};
+      float lo4[4], hi4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // kh = 0 holds column c, the partner c + 256; kh = 1 the reverse
+        const float own = k0 ? z[4 * i + e] : z[64 + 4 * i + e];
+        lo4[e] = k0 ? own + o4[e] : o4[e] + own;
+        hi4[e] = k0 ? own - o4[e] : o4[e] - own;
+      }
+      const int cb = (k0 ? 0 : 4) + i / 4, j4 = i % 4;
+      const int col = 32 * cb + 8 * j4 + 4 * half;
+      *reinterpret_cast<float4*>(out + col) = make_float4(lo4[0], lo4[1], lo4[2], lo4[3]);
+      *reinterpret_cast<float4*>(out + col + 256) = make_float4(hi4[0], hi4[1], hi4[2], hi4[3]);
+    }
+  }
+  if (a.direct_lse != nullptr && half == 0 && kh == 0)
+    a.direct_lse[static_cast<int64_t>(b) * a.heads + head] = (m_ref + log2f(l_tot)) * kLn2;
+}
+
+template <int W, int DR, int HB, int KS, int STQ, int LAYOUT, bool DIRECT>
 __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decode_mfma_kernel(DecodeLaunch a, float scale_log2, int units,
                                                                        int members, int page_shift) {
   using C = Cfg<W, DR, HB, KS, STQ, LAYOUT>;
@@ -157,6 +263,7 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
   for (;;) {
   int b, t_begin, t_end;
   int64_t part_row0;  // partial row of head 0 of this segment
+  bool whole = false;  // the segment is its row's whole context (balanced schedule)
   if (a.sched == 0) {
     const int c = u % a.num_chunks;
     b = u / a.num_chunks;
@@ -179,6 +286,7 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
     t_begin = static_cast<int>((g_next - p0) * kNT);
     t_end = min(a.seq_lens[b], static_cast<int>((seg_end - p0) * kNT));
     part_row0 = ((static_cast<int64_t>(b) + u) * a.shard_count + s_local) * a.heads;
+    whole = g_next == p0 && seg_end == p1;
     g_next = seg_end;
   }
   const int n_tiles = (t_end - t_begin + kNT - 1) / kNT;
@@ -715,6 +823,18 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
 
   // Chunk result: o = O / l, lse = ln 2 * (m + log2 l); the two lane halves hold disjoint tokens.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // A separate instantiation (DIRECT) carries this, so that the decode kernels' registers are
+  // allocated without it.
+  if constexpr (DIRECT) {
+    static_assert(direct_rows(W, KS), "tiles that finish rows");
+    static_assert(C::NWAVES * 16384 <= C::ST * C::TILE_BYTES, "the row exchange fits in the ring");
+    if (whole && a.direct_out != nullptr) {  // workgroup-uniform
+      finish_row<C::CB>(o_acc, l_tot, m_ref, a, b, head, kh, half, lane, lds + static_cast<size_t>(wv) * 16384,
+                        lds + static_cast<size_t>(wv ^ 1) * 16384);
+      __syncthreads();  // the next segment reuses the ring, which held the exchange
+      continue;
+    }
+  }
   const float inv = 1.0f / l_tot;
   const int64_t part = part_row0 + head;
   float* dst = a.part_o + part * W;
@@ -738,7 +858,9 @@ __global__ __launch_bounds__(HB * KS * 64, waves_per_simd(W, HB, KS)) void decod
 template <int W, int DR, int HB, int KS, int STQ, int LAYOUT>
 hipError_t launch_one(const DecodeLaunch& a, hipStream_t stream) {
   using C = Cfg<W, DR, HB, KS, STQ, LAYOUT>;
-  auto kern = decode_mfma_kernel<W, DR, HB, KS, STQ, LAYOUT>;
+  auto kern = decode_mfma_kernel<W, DR, HB, KS, STQ, LAYOUT, false>;
+  if constexpr (direct_rows(W, KS))
+    if (a.direct_out != nullptr) kern = decode_mfma_kernel<W, DR, HB, KS, STQ, LAYOUT, true>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      C::LDS_BYTES);
   if (e != hipSuccess) return e;
@@ -816,6 +938,8 @@ void mfma_plan_info(int w, int heads, int* head_groups, int* wgs_per_cu) {
 }
 
 int mfma_max_chunk_pages() { return kMaxPages - 2; }
+
+bool mfma_direct_rows(int w) { return direct_rows(w, tile_cfg(w).ks); }
 
 int mfma_max_segment_pages() { return kMaxPages - 2; }
 

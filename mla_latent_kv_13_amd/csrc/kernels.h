@@ -39,6 +39,14 @@ struct DecodeLaunch {
   const int* row_seq;
   // XCDs of the device: consecutive workgroup ids are dispatched to the XCDs in turn.
   int xcds;
+  // Rows finished in the kernel (balanced schedule, one shard of the whole latent, MFMA kernels
+  // for which mfma_direct_rows() holds; null otherwise): a row whose tiles all fall in one
+  // worker's share gets its final output written here, [batch, heads, d_latent] (rotated back by
+  // H when direct_wht), and its log-sum-exp to direct_lse [batch, heads] (may be null), instead
+  // of a partial; the merge then leaves that row alone (MergeLaunch::skip_whole).
+  float* direct_out;
+  float* direct_lse;
+  int direct_wht;
 };
 
 struct MergeLaunch {
@@ -53,6 +61,9 @@ struct MergeLaunch {
   int wht;
   float* out;
   float* lse;   // may be null
+  // 1: rows whose tiles all fall in one worker's share were finished by the decode kernel
+  // (DecodeLaunch::direct_out) and are skipped (balanced schedule only)
+  int skip_whole;
 };
 
 // dtype: 0 = fp32, 1 = bf16 storage.
@@ -76,6 +87,8 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, hipStream_t stream);
 void mfma_plan_info(int w, int heads, int* head_groups, int* wgs_per_cu);
 // Largest number of cache pages one chunk of the MFMA kernel may span.
 int mfma_max_chunk_pages();
+// Whether the MFMA kernel of value width w finishes whole rows itself (DecodeLaunch::direct_out).
+bool mfma_direct_rows(int w);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 // The merge with the value up-projection fused in: out_v[b,h,:] = W_UV[h] . (the row launch_merge
 // would write to a.out, which is not written); bf16 weights [heads, d_v, d_latent], d_latent a

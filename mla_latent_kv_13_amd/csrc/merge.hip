@@ -255,6 +255,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeLaunch a) {
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.x * kMergeWaves + wv, b = blockIdx.y;
   if (h >= a.heads) return;  // the rest of this kernel is wave-local
+  if (a.skip_whole && a.sched == 1) {
+    // rows whose tiles all fall in one worker's share were finished by the decode kernel (the
+    // same share boundaries as its segments: worker w takes tiles [w*total/nw, (w+1)*total/nw))
+    const int64_t total = a.tile_prefix[a.batch];
+    const int64_t p0 = a.tile_prefix[b], p1 = a.tile_prefix[b + 1];
+    const int64_t nw = min(static_cast<int64_t>(a.workers), total);
+    if (p1 > p0 && ((p0 + 1) * nw - 1) / total == (p1 * nw - 1) / total) return;
+  }
   float* y = ybuf[wv];
   merge_row<V, E, P, S>(a, b, h, lane, y);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // this wave's LDS row is complete
