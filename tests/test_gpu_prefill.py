@@ -126,6 +126,27 @@ def test_full_size_chunked_prefill_step_sampled():
         assert_lse(got_lse[r:r + 1], ref_lse, "bf16", f"row {r}", "wht")
 
 
+@pytest.mark.parametrize("transform", ["wht", "identity"])
+def test_prefill_rows_finished_whole_and_merged(transform):
+    """Under the balanced schedule a row whose tiles all fall in one workgroup's share is finished by
+    the decode kernel itself (normalised, rotated back, written), and the merge combines the others.
+    One sequence gives a single row over 20,000 tokens, longer than any share, so it is split and
+    merged; the other gives 400 short rows, most of them inside one share.  Every row against the
+    oracle, and the chunked schedule (every row merged) on the same inputs against it too."""
+    case = inputs.make_case(131, batch=2, heads=64, d_latent=512, d_rope=64, shards=1, lens=[20000, 400],
+                            paged=True, page_size=64, transform=transform, scale=1.0 / np.sqrt(192), extra_pages=1,
+                            name=f"prefill-whole-and-split-{transform}")
+    dc = DeviceCase(case)
+    query_start, q_lat, q_rope = _queries(case, 132, [1, 400])
+    ref, ref_lse = _oracle(case, query_start, q_lat, q_rope)
+    for schedule in ("balanced", "chunked"):
+        print(f"prefill {transform} {schedule}", flush=True)
+        out, lse = _prefill(dc, query_start, q_lat, q_rope, schedule=schedule)
+        torch.cuda.synchronize()
+        assert_parity(out.cpu().numpy(), ref, "bf16", f"{transform} {schedule}")
+        assert_lse(lse.cpu().numpy(), ref_lse, "bf16", f"{transform} {schedule}", transform)
+
+
 def _random_prefill(i):
     rng = np.random.default_rng([4241, i])
     dtype = "f32" if rng.random() < 0.15 else "bf16"
