@@ -80,14 +80,27 @@ def merge_slots(b, workers, seq_lens):
     return [b + w for w in range(worker_of(p0), worker_of(p1 - 1) + 1)]
 
 
+def merge_skips(b, workers, seq_lens):
+    """The merge's rule for rows the decode kernel finishes itself (prefill): the sequence's first
+    and last tiles fall in the same worker's share."""
+    prefix = tile_prefix(seq_lens)
+    total = int(prefix[-1])
+    nw = min(workers, total)
+    p0, p1 = int(prefix[b]), int(prefix[b + 1])
+    return p1 > p0 and ((p0 + 1) * nw - 1) // total == (p1 * nw - 1) // total
+
+
 def check_partition(seq_lens, workers):
     batch = len(seq_lens)
     prefix = tile_prefix(seq_lens)
     total = int(prefix[-1])
     covered = np.zeros(total, dtype=np.int64)
     written = {}
+    whole = set()  # sequences the decode kernel finishes: one segment from first to last tile
     for u in range(workers):
         for b, t0, t1, g0, g1, slot in walk_worker(u, workers, seq_lens):
+            if g0 == prefix[b] and g1 == prefix[b + 1]:
+                whole.add(b)
             covered[g0:g1] += 1
             assert slot not in written, "two segments write one partial slot"
             assert 0 <= slot < batch + workers, "slot outside the workspace"
@@ -103,6 +116,10 @@ def check_partition(seq_lens, workers):
         assert pos == seq_lens[b]
         # the merge reads exactly the slots the kernel wrote for b
         assert sorted(s for s, (bb, _, _) in written.items() if bb == b) == merge_slots(b, workers, seq_lens)
+        # the kernel finishes b itself exactly when the merge skips it, and then b is one segment
+        assert (b in whole) == merge_skips(b, workers, seq_lens)
+        if b in whole:
+            assert len(spans) == 1
 
 
 RAGGED = [
