@@ -169,7 +169,7 @@ def _random_prefill(i):
     return kw, new, schedule
 
 
-@pytest.mark.parametrize("i", range(20))
+@pytest.mark.parametrize("i", range(60))
 def test_random_prefill_configuration(i):
     kw, new, schedule = _random_prefill(i)
     print(f"prefill config {i}: {kw} new {new} schedule {schedule}", flush=True)

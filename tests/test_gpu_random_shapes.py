@@ -42,7 +42,7 @@ def _config(i):
                 extra_pages=int(rng.integers(1, 3)) if paged else 0), shard_begin, shard_count, schedule
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(100))
 def test_random_configuration(i):
     kw, s0, n, schedule = _config(i)
     print(f"config {i}: {kw} shards [{s0}, {s0 + n}) schedule {schedule}", flush=True)
