@@ -155,6 +155,32 @@ def test_bitwise_deterministic():
         assert torch.equal(first, again) and torch.equal(first_lse, again_lse)
 
 
+def test_calls_on_two_streams_at_once():
+    """The library keeps no state between calls: calls enqueued on two streams at once, each with its
+    own outputs and workspace (a paged rotated G = 2 decode with the balanced schedule, a contiguous
+    G = 1 decode with chunks), give the same bits as the same calls one after the other."""
+    ca = inputs.make_case(12, batch=4, heads=128, d_latent=512, d_rope=64, shards=2, lens=[3000, 70, 0, 1500],
+                          paged=True, page_size=64, transform="wht", extra_pages=2)
+    cb = inputs.make_case(13, batch=3, heads=64, d_latent=512, d_rope=64, shards=1, lens=[2048, 1, 777])
+    da, db = DeviceCase(ca), DeviceCase(cb)
+    ref_a, ref_b = da.decode(), db.decode()
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            oa = da.decode()
+        with torch.cuda.stream(sb):
+            ob = db.decode()
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert torch.equal(oa[0], ref_a[0]) and torch.equal(oa[1], ref_a[1])
+        assert torch.equal(ob[0], ref_b[0]) and torch.equal(ob[1], ref_b[1])
+
+
 BALANCED = [
     ("contig_ragged_g2", dict(batch=5, heads=128, shards=2, lens=[1000, 0, 1, 4097, 33])),
     ("paged_ragged_g1", dict(batch=4, heads=128, shards=1, lens=[2500, 31, 0, 700], paged=True, page_size=64,
